@@ -1,0 +1,330 @@
+"""Pins that tie the fp64 oracle to facts other than itself.
+
+Each pin takes an attention implementation ``impl(q, k, v, causal=,
+seqused_k=, scale=) -> (out, lse)`` (numpy in, numpy out) and raises
+AssertionError when the implementation disagrees with:
+
+* closed forms (single key, equal logits, two keys),
+* a pure-Python brute force in 50-digit mpmath on tiny inputs,
+* invariants the definition implies (padding is never read, key
+  permutation, shift of all keys, linearity in V, GQA equals MHA with
+  replicated K/V, causal row i equals non-causal attention over keys 0..i),
+* numerical stability at logits of size 1e4 (against mpmath).
+
+The same pins run against the oracle and against mutants of it with a
+planted mistake (tests/test_oracle_pins.py), which shows that each kind of
+plausible mistake is caught by at least one pin.
+"""
+
+from __future__ import annotations
+
+import math
+
+import mpmath
+import numpy as np
+
+mpmath.mp.dps = 50
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _randn(rng, *shape):
+    # Values with few mantissa bits, as bf16 inputs have.
+    return np.round(rng.standard_normal(shape) * 64.0) / 64.0
+
+
+def brute_force(q, k, v, *, causal=False, seqused_k=None, scale=None):
+    """Attention by nested loops in 50-digit mpmath (tiny inputs only).
+
+    Written without numpy arithmetic: every dot product, exponential and sum
+    is an mpmath operation, so it shares no rounding or library routine with
+    the oracle.
+    """
+    B, Sq, Hq, D = q.shape
+    _, Sk, Hkv, _ = k.shape
+    sigma = mpmath.mpf(float(np.float32(1.0 / math.sqrt(D) if scale is None else scale)))
+    g = Hq // Hkv
+    out = np.zeros((B, Sq, Hq, D))
+    lse = np.zeros((B, Hq, Sq))
+    for b in range(B):
+        nb = Sk if seqused_k is None else max(0, min(int(seqused_k[b]), Sk))
+        for h in range(Hq):
+            hk = h // g
+            for i in range(Sq):
+                keys = [j for j in range(nb) if (not causal or j <= i)]
+                if not keys:
+                    lse[b, h, i] = -math.inf
+                    continue
+                s = {j: sigma * mpmath.fsum(mpmath.mpf(float(q[b, i, h, d])) * mpmath.mpf(float(k[b, j, hk, d]))
+                                            for d in range(D)) for j in keys}
+                total = mpmath.fsum(mpmath.exp(s[j]) for j in keys)
+                lse[b, h, i] = float(mpmath.log(total))
+                for d in range(D):
+                    num = mpmath.fsum(mpmath.exp(s[j]) * mpmath.mpf(float(v[b, j, hk, d])) for j in keys)
+                    out[b, i, h, d] = float(num / total)
+    return out, lse
+
+
+def _close(a, b, atol, rtol=0.0, what=""):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} != {b.shape}"
+    fin = np.isfinite(b)
+    assert np.array_equal(np.isfinite(a), fin), f"{what}: non-finite pattern differs"
+    assert np.array_equal(a[~fin], b[~fin]), f"{what}: infinities differ"
+    err = np.abs(a[fin] - b[fin])
+    lim = atol + rtol * np.abs(b[fin])
+    assert np.all(err <= lim), f"{what}: max err {err.max() if err.size else 0}"
+
+
+# ---------------------------------------------------------------- closed forms
+
+def pin_single_key(impl):
+    """One key: out = v0 exactly, lse = sigma * q . k0."""
+    rng = _rng(11)
+    for (Hq, Hkv, D) in [(1, 1, 8), (4, 2, 16), (3, 1, 5)]:
+        q = _randn(rng, 2, 3, Hq, D)
+        k = _randn(rng, 2, 1, Hkv, D)
+        v = _randn(rng, 2, 1, Hkv, D)
+        out, lse = impl(q, k, v, scale=0.25)
+        g = Hq // Hkv
+        for b in range(2):
+            for i in range(3):
+                for h in range(Hq):
+                    assert np.array_equal(out[b, i, h], v[b, 0, h // g]), "single key: out != v0"
+                    s0 = 0.25 * math.fsum(q[b, i, h, d] * k[b, 0, h // g, d] for d in range(D))
+                    assert abs(lse[b, h, i] - s0) <= 1e-12 * max(1.0, abs(s0)), "single key: lse != s0"
+
+
+def pin_equal_logits(impl):
+    """q = 0: every logit is 0, so lse = ln n and out = mean of the valid v."""
+    rng = _rng(12)
+    B, S, Sk, H, D = 2, 5, 9, 2, 6
+    q = np.zeros((B, S, H, D))
+    k = _randn(rng, B, Sk, H, D)
+    v = _randn(rng, B, Sk, H, D)
+    seq = np.array([9, 4])
+    out, lse = impl(q, k, v, seqused_k=seq)
+    for b in range(B):
+        n = int(seq[b])
+        for h in range(H):
+            for i in range(S):
+                assert abs(lse[b, h, i] - math.log(n)) <= 1e-13, "equal logits: lse != ln n"
+                for d in range(D):
+                    mean = math.fsum(v[b, j, h, d] for j in range(n)) / n
+                    assert abs(out[b, i, h, d] - mean) <= 1e-13, "equal logits: out != mean(v)"
+    # Equal keys instead of zero queries: lse = ln n + sigma * q . k
+    kk = np.broadcast_to(_randn(rng, 1, 1, H, D), (B, Sk, H, D)).copy()
+    q2 = _randn(rng, B, S, H, D)
+    out2, lse2 = impl(q2, kk, v, scale=0.5)
+    for b in range(B):
+        for h in range(H):
+            for i in range(S):
+                s = 0.5 * math.fsum(q2[b, i, h, d] * kk[0, 0, h, d] for d in range(D))
+                assert abs(lse2[b, h, i] - (math.log(Sk) + s)) <= 1e-12 * max(1, abs(s)), "equal keys: lse"
+
+
+def pin_two_keys(impl):
+    """Two keys: lse = log(e^s0 + e^s1); out = sig(s0-s1) v0 + sig(s1-s0) v1."""
+    rng = _rng(13)
+    D = 4
+    q = _randn(rng, 1, 2, 1, D) * 3
+    k = _randn(rng, 1, 2, 1, D)
+    v = _randn(rng, 1, 2, 1, D)
+    out, lse = impl(q, k, v, scale=1.0)
+    for i in range(2):
+        s0 = mpmath.fsum(mpmath.mpf(q[0, i, 0, d]) * mpmath.mpf(k[0, 0, 0, d]) for d in range(D))
+        s1 = mpmath.fsum(mpmath.mpf(q[0, i, 0, d]) * mpmath.mpf(k[0, 1, 0, d]) for d in range(D))
+        assert abs(lse[0, 0, i] - float(mpmath.log(mpmath.exp(s0) + mpmath.exp(s1)))) <= 1e-13
+        w0 = 1 / (1 + mpmath.exp(s1 - s0))
+        w1 = 1 / (1 + mpmath.exp(s0 - s1))
+        for d in range(D):
+            want = float(w0 * mpmath.mpf(v[0, 0, 0, d]) + w1 * mpmath.mpf(v[0, 1, 0, d]))
+            assert abs(out[0, i, 0, d] - want) <= 1e-13, "two keys: out"
+
+
+def pin_empty(impl):
+    """No attended key (seqused_k = 0): out = 0 and lse = -inf."""
+    rng = _rng(14)
+    q = _randn(rng, 2, 3, 2, 4)
+    k = _randn(rng, 2, 5, 1, 4)
+    v = _randn(rng, 2, 5, 1, 4)
+    out, lse = impl(q, k, v, seqused_k=np.array([0, 2]))
+    assert np.all(out[0] == 0.0), "empty: out != 0"
+    assert np.all(np.isneginf(lse[0])), "empty: lse != -inf"
+    assert np.all(np.isfinite(lse[1])), "non-empty row must be finite"
+
+
+# ------------------------------------------------------------------ brute force
+
+def pin_brute_force(impl, cases=None):
+    """Agreement with the mpmath brute force on tiny shapes, 1e-12."""
+    rng = _rng(15)
+    if cases is None:
+        cases = [
+            dict(B=1, Sq=3, Sk=4, Hq=1, Hkv=1, D=3, causal=False, seq=None),
+            dict(B=2, Sq=4, Sk=4, Hq=4, Hkv=2, D=5, causal=True, seq=None),
+            dict(B=2, Sq=3, Sk=6, Hq=2, Hkv=1, D=4, causal=False, seq=[6, 2]),
+            dict(B=1, Sq=5, Sk=5, Hq=3, Hkv=3, D=2, causal=True, seq=None),
+        ]
+    for c in cases:
+        q = _randn(rng, c["B"], c["Sq"], c["Hq"], c["D"])
+        k = _randn(rng, c["B"], c["Sk"], c["Hkv"], c["D"])
+        v = _randn(rng, c["B"], c["Sk"], c["Hkv"], c["D"])
+        seq = None if c["seq"] is None else np.array(c["seq"])
+        if seq is not None:
+            for b in range(c["B"]):
+                k[b, seq[b]:] = 1e4
+                v[b, seq[b]:] = 1e4
+        got = impl(q, k, v, causal=c["causal"], seqused_k=seq, scale=0.7)
+        want = brute_force(q, k, v, causal=c["causal"], seqused_k=seq, scale=0.7)
+        _close(got[0], want[0], 1e-12, what=f"brute out {c}")
+        _close(got[1], want[1], 1e-12, what=f"brute lse {c}")
+
+
+# ------------------------------------------------------------------- invariants
+
+def pin_padding_never_read(impl):
+    """Garbage (1e4, +inf, nan) past seqused_k changes nothing: the result is
+    exactly that of the buffer truncated to the valid length."""
+    rng = _rng(16)
+    B, Sq, Sk, Hq, Hkv, D = 2, 4, 9, 4, 1, 6
+    q = _randn(rng, B, Sq, Hq, D)
+    k = _randn(rng, B, Sk, Hkv, D)
+    v = _randn(rng, B, Sk, Hkv, D)
+    seq = np.array([7, 3])
+    for poison in (1e4, np.inf, np.nan, -1e4):
+        kp, vp = k.copy(), v.copy()
+        for b in range(B):
+            kp[b, seq[b]:] = poison
+            vp[b, seq[b]:] = poison
+        out, lse = impl(q, kp, vp, seqused_k=seq)
+        for b in range(B):
+            n = int(seq[b])
+            ob, lb = impl(q[b:b + 1], k[b:b + 1, :n], v[b:b + 1, :n])
+            assert np.array_equal(out[b:b + 1], ob), f"padding {poison} leaked into out"
+            assert np.array_equal(lse[b:b + 1], lb), f"padding {poison} leaked into lse"
+
+
+def pin_key_permutation(impl):
+    """Non-causal: permuting K and V rows together leaves the result unchanged."""
+    rng = _rng(17)
+    q = _randn(rng, 1, 5, 2, 7)
+    k = _randn(rng, 1, 11, 2, 7)
+    v = _randn(rng, 1, 11, 2, 7)
+    p = rng.permutation(11)
+    o1, l1 = impl(q, k, v)
+    o2, l2 = impl(q, k[:, p], v[:, p])
+    _close(o2, o1, 1e-13, what="permutation out")
+    _close(l2, l1, 1e-13, what="permutation lse")
+
+
+def pin_key_shift(impl):
+    """k_j -> k_j + u for all j: out unchanged, lse_i + sigma * q_i . u."""
+    rng = _rng(18)
+    q = _randn(rng, 1, 4, 2, 5)
+    k = _randn(rng, 1, 6, 2, 5)
+    v = _randn(rng, 1, 6, 2, 5)
+    u = _randn(rng, 5)
+    o1, l1 = impl(q, k, v, scale=0.5)
+    o2, l2 = impl(q, k + u, v, scale=0.5)
+    _close(o2, o1, 1e-12, what="shift out")
+    shift = 0.5 * np.einsum("bihd,d->bhi", q, u)
+    _close(l2, l1 + shift, 1e-12, what="shift lse")
+
+
+def pin_v_linearity(impl):
+    """out is linear in V; lse does not depend on V."""
+    rng = _rng(19)
+    q = _randn(rng, 1, 4, 2, 5)
+    k = _randn(rng, 1, 6, 1, 5)
+    v1 = _randn(rng, 1, 6, 1, 5)
+    v2 = _randn(rng, 1, 6, 1, 5)
+    o1, l1 = impl(q, k, v1)
+    o2, l2 = impl(q, k, v2)
+    o3, l3 = impl(q, k, 2.0 * v1 - 3.0 * v2)
+    _close(o3, 2.0 * o1 - 3.0 * o2, 1e-12, what="linearity")
+    assert np.array_equal(l1, l2) and np.array_equal(l1, l3), "lse depends on V"
+
+
+def pin_gqa_is_replicated_mha(impl):
+    """GQA(Hq, Hkv) equals MHA(Hq, Hq) with each K/V head repeated Hq/Hkv
+    times in place (heads h = hk*g .. hk*g+g-1 read K/V head hk)."""
+    rng = _rng(20)
+    for (Hq, Hkv) in [(4, 2), (8, 1), (6, 3)]:
+        g = Hq // Hkv
+        q = _randn(rng, 2, 3, Hq, 4)
+        k = _randn(rng, 2, 5, Hkv, 4)
+        v = _randn(rng, 2, 5, Hkv, 4)
+        o1, l1 = impl(q, k, v)
+        o2, l2 = impl(q, np.repeat(k, g, axis=2), np.repeat(v, g, axis=2))
+        _close(o1, o2, 1e-13, what=f"gqa out {Hq}/{Hkv}")
+        _close(l1, l2, 1e-13, what=f"gqa lse {Hq}/{Hkv}")
+
+
+def pin_causal_prefix(impl):
+    """Causal row 0 equals v0; causal row i equals non-causal attention over
+    keys 0..i."""
+    rng = _rng(21)
+    S = 6
+    q = _randn(rng, 1, S, 2, 4)
+    k = _randn(rng, 1, S, 1, 4)
+    v = _randn(rng, 1, S, 1, 4)
+    out, lse = impl(q, k, v, causal=True)
+    for h in range(2):
+        assert np.array_equal(out[0, 0, h], v[0, 0, 0]), "causal row 0 != v0"
+    for i in range(S):
+        oi, li = impl(q[:, i:i + 1], k[:, :i + 1], v[:, :i + 1])
+        _close(out[:, i:i + 1], oi, 1e-13, what=f"causal row {i} out")
+        _close(lse[:, :, i:i + 1], li, 1e-13, what=f"causal row {i} lse")
+
+
+def pin_scale(impl):
+    """The logits are sigma * q.k with sigma = float32(scale); the default
+    scale is 1/sqrt(D)."""
+    rng = _rng(22)
+    q = _randn(rng, 1, 3, 1, 16)
+    k = _randn(rng, 1, 5, 1, 16)
+    v = _randn(rng, 1, 5, 1, 16)
+    o1, l1 = impl(q, k, v)
+    o2, l2 = impl(q, k, v, scale=0.25)  # 1/sqrt(16), exact
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2), "default scale != 1/sqrt(D)"
+    o3, l3 = impl(q * 0.25, k, v, scale=1.0)  # power-of-two scale is exact
+    _close(o3, o2, 1e-14, what="scale multiplies logits (out)")
+    _close(l3, l2, 1e-14, what="scale multiplies logits (lse)")
+    o4, l4 = impl(q, k, v, scale=0.1)
+    o5, l5 = impl(q, k, v, scale=float(np.float32(0.1)))
+    assert np.array_equal(o4, o5) and np.array_equal(l4, l5), "scale is not rounded to float32"
+
+
+def pin_large_logits(impl):
+    """Logits of magnitude ~1e4 (exp overflows without the max shift):
+    agreement with 50-digit mpmath."""
+    rng = _rng(23)
+    q = _randn(rng, 1, 3, 1, 4) * 100
+    k = _randn(rng, 1, 5, 1, 4) * 100
+    v = _randn(rng, 1, 5, 1, 4)
+    out, lse = impl(q, k, v, scale=1.0)
+    want = brute_force(q, k, v, scale=1.0)
+    assert np.all(np.abs(lse) > 100), "test needs large logits"
+    _close(out, want[0], 1e-12, what="large logits out")
+    _close(lse, want[1], 0.0, rtol=1e-14, what="large logits lse")
+
+
+ALL_PINS = [
+    pin_single_key,
+    pin_equal_logits,
+    pin_two_keys,
+    pin_empty,
+    pin_brute_force,
+    pin_padding_never_read,
+    pin_key_permutation,
+    pin_key_shift,
+    pin_v_linearity,
+    pin_gqa_is_replicated_mha,
+    pin_causal_prefix,
+    pin_scale,
+    pin_large_logits,
+]
