@@ -1,0 +1,30 @@
+"""Fused attention forward for AMD Instinct MI355X (gfx950).
+
+The compute path is the HIP library built from ``csrc/`` (C ABI in
+``include/fa.h``); ``attention_forward_amd.fa`` is its ctypes binding.  The
+library is loaded on first use and its absence is an error.
+"""
+
+from .fa import (  # noqa: F401
+    FA_OK,
+    FAError,
+    attention,
+    fa_abi_version,
+    fa_fwd,
+    fa_fwd_workspace_bytes,
+    fa_set_workspace,
+    fa_status_string,
+    load_library,
+)
+
+__all__ = [
+    "FA_OK",
+    "FAError",
+    "attention",
+    "fa_abi_version",
+    "fa_fwd",
+    "fa_fwd_workspace_bytes",
+    "fa_set_workspace",
+    "fa_status_string",
+    "load_library",
+]

@@ -1,0 +1,168 @@
+"""Python binding of the C ABI in include/fa.h (ctypes; argument marshalling only).
+
+The functions ``fa_fwd``, ``fa_fwd_workspace_bytes``, ``fa_set_workspace``,
+``fa_status_string`` and ``fa_abi_version`` mirror the C entry points one to
+one and take plain integers for device pointers and streams.  ``attention``
+is the tensor-level convenience on top: it checks the torch tensors, takes
+the current HIP stream, registers a split-KV workspace when the shape needs
+one, allocates ``out``/``lse`` only when they are not passed (the
+allocation-free form is the one with both passed), and raises on any error
+code.  Every arithmetic step runs in the HIP kernels; there is no other
+implementation to fall back to.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa_mi355x.so")
+
+FA_OK = 0
+FA_ERR_NULL = 1
+FA_ERR_SHAPE = 2
+FA_ERR_UNSUPPORTED = 3
+FA_ERR_ALIGN = 4
+FA_ERR_SCALE = 5
+FA_ERR_WORKSPACE = 6
+FA_ERR_LAUNCH = 7
+FA_ERR_ALIAS = 8
+
+EXPORTS = ("fa_fwd", "fa_fwd_workspace_bytes", "fa_set_workspace", "fa_status_string", "fa_abi_version")
+
+_lib = None
+_lib_lock = threading.Lock()
+
+
+class FAError(RuntimeError):
+    """An FA_ERR_* status returned by the library."""
+
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {fa_status_string(code)} (code {code})")
+
+
+def load_library():
+    """Load the built HIP library (raises if it has not been built)."""
+    global _lib
+    with _lib_lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it with `python -m attention_forward_amd.build` "
+                "(there is no other implementation of the attention path)")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+        lib.fa_fwd.restype = i32
+        lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, f32, vp]
+        lib.fa_fwd_workspace_bytes.restype = ctypes.c_size_t
+        lib.fa_fwd_workspace_bytes.argtypes = [i32] * 7
+        lib.fa_set_workspace.restype = i32
+        lib.fa_set_workspace.argtypes = [vp, ctypes.c_size_t]
+        lib.fa_status_string.restype = ctypes.c_char_p
+        lib.fa_status_string.argtypes = [i32]
+        lib.fa_abi_version.restype = i32
+        lib.fa_abi_version.argtypes = []
+        _lib = lib
+        return lib
+
+
+# ------------------------------------------------------------ raw C entry points
+
+def fa_fwd(q, k, v, out, lse, B, Sq, Sk, Hq, Hkv, D, causal, seqused_k, scale, stream) -> int:
+    """C ``fa_fwd``; pointers and stream are integers (0 for NULL)."""
+    return load_library().fa_fwd(q or None, k or None, v or None, out or None, lse or None,
+                                 B, Sq, Sk, Hq, Hkv, D, int(causal), seqused_k or None,
+                                 ctypes.c_float(scale), stream or None)
+
+
+def fa_fwd_workspace_bytes(B, Sq, Sk, Hq, Hkv, D, causal) -> int:
+    return int(load_library().fa_fwd_workspace_bytes(B, Sq, Sk, Hq, Hkv, D, int(causal)))
+
+
+def fa_set_workspace(dev_ptr, nbytes) -> int:
+    return load_library().fa_set_workspace(dev_ptr or None, nbytes)
+
+
+def fa_status_string(code: int) -> str:
+    return load_library().fa_status_string(code).decode()
+
+
+def fa_abi_version() -> int:
+    return load_library().fa_abi_version()
+
+
+# ------------------------------------------------------------- tensor interface
+
+_workspaces = {}  # device index -> registered torch buffer
+
+
+def ensure_workspace(device, nbytes: int):
+    """Register a workspace of at least ``nbytes`` on ``device`` (torch memory)."""
+    import torch
+
+    if nbytes <= 0:
+        return None
+    idx = device.index if device.index is not None else torch.cuda.current_device()
+    buf = _workspaces.get(idx)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=torch.device("cuda", idx))
+        with torch.cuda.device(idx):
+            rc = fa_set_workspace(buf.data_ptr(), buf.numel())
+        if rc != FA_OK:
+            raise FAError(rc, "fa_set_workspace")
+        _workspaces[idx] = buf
+    return buf
+
+
+def attention(q, k, v, *, causal=False, seqused_k=None, scale=None, out=None, lse=None,
+              return_lse=True):
+    """out, lse = softmax(scale * q k^T + mask) v for bf16 BSHD cuda tensors.
+
+    q [B, Sq, Hq, D]; k, v [B, Sk, Hkv, D]; seqused_k int32 [B] on the same
+    device or None.  ``scale`` defaults to 1/sqrt(D).  Returns (out, lse)
+    with lse [B, Hq, Sq] float32 (None when ``return_lse`` is False and no
+    ``lse`` tensor is passed).
+    """
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or not t.is_cuda:
+            raise TypeError(f"{name} must be a bfloat16 cuda tensor")
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 4-D (batch, seq, heads, head_dim) tensor")
+    B, Sq, Hq, D = q.shape
+    Bk, Sk, Hkv, Dk = k.shape
+    if tuple(v.shape) != tuple(k.shape) or Bk != B or Dk != D:
+        raise ValueError("k and v must be [B, Sk, Hkv, D] matching q")
+    dev = q.device
+    if k.device != dev or v.device != dev:
+        raise ValueError("q, k, v must be on one device")
+    if seqused_k is not None:
+        if seqused_k.dtype != torch.int32 or seqused_k.device != dev or seqused_k.numel() != B \
+                or not seqused_k.is_contiguous():
+            raise ValueError("seqused_k must be a contiguous int32 tensor of B entries on q's device")
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != torch.bfloat16 or out.device != dev or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 tensor shaped like q")
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev)
+    elif lse is not None and (tuple(lse.shape) != (B, Hq, Sq) or lse.dtype != torch.float32
+                              or lse.device != dev or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 [B, Hq, Sq] tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    causal = bool(causal)
+    with torch.cuda.device(dev):
+        ensure_workspace(dev, fa_fwd_workspace_bytes(B, Sq, Sk, Hq, Hkv, D, causal))
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        rc = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                    0 if lse is None else lse.data_ptr(), B, Sq, Sk, Hq, Hkv, D, causal,
+                    0 if seqused_k is None else seqused_k.data_ptr(), float(scale), stream)
+    if rc != FA_OK:
+        raise FAError(rc, "fa_fwd")
+    return out, lse

@@ -1,0 +1,261 @@
+#!/usr/bin/env python3
+"""Throughput of the fused attention forward on one MI355X.
+
+One step = one fa_fwd call (the whole hot path: validation, launch, GQA
+packing, K/V streaming, QK^T, masking, online softmax, PV, epilogue, and the
+split-KV merge where the shape takes that path) over one batch of seeded
+synthetic inputs that are already resident in HBM.
+
+The K timed steps are captured back to back in one HIP graph and replayed
+once between two synchronisations, so host launch cost is not counted; the
+kernel time per launch comes from HIP events recorded on the launch stream
+around that replay.  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd effective TFLOP/s (valid keys) + µs/call; % of MFMA/HBM roofline"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 4096 FLOP/clk x 2.4 GHz)
+DEFAULT_WORKLOAD = "vit_multiview"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["attention_forward_amd/csrc/fa_kernels.hip", "attention_forward_amd/csrc/fa_api.cpp",
+                  "attention_forward_amd/csrc/fa_launch.h"]
+
+
+def kernel_sha() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic(w):
+    """Algorithmic FLOPs and HBM bytes of one call: 4*D per attended
+    (query, key) pair; bytes = Q + valid K + valid V + out (bf16) + lse (fp32)."""
+    n = w.valid_keys
+    if w.causal:
+        pairs = w.B * w.Hq * sum(min(i + 1, n) for i in range(w.Sq))
+    else:
+        pairs = w.B * w.Hq * w.Sq * n
+    flops = 4 * w.D * pairs
+    qo = w.B * w.Sq * w.Hq * w.D * 2
+    kv = w.B * n * w.Hkv * w.D * 2
+    lse = w.B * w.Hq * w.Sq * 4
+    return flops, 2 * qo + 2 * kv + lse
+
+
+def binding_roofline(flops, nbytes):
+    """'mfma' when the arithmetic intensity is above the ridge point, else 'hbm'."""
+    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    return "mfma" if flops / nbytes > ridge else "hbm"
+
+
+def roofline_entry(bound, flops, nbytes, sec_per_launch, traffic=None):
+    if bound == "mfma":
+        achieved = flops / sec_per_launch / 1e12
+        return {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 5), "traffic": traffic}
+    achieved = nbytes / sec_per_launch / 1e9
+    return {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 5), "traffic": traffic}
+
+
+def load_traffic(workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary,
+    only if it was taken on the current kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(workload)
+    if not e or e.get("kernel_sha") != kernel_sha():
+        return None
+    return e.get("bytes_per_launch")
+
+
+class Runner:
+    """Device-resident inputs and preallocated outputs for one workload."""
+
+    def __init__(self, w, device):
+        import torch
+        from attention_forward_amd import fa
+        from attention_forward_amd.workloads import make_inputs
+
+        self.w = w
+        self.fa = fa
+        q, k, v, s = make_inputs(w.name)
+        self.q, self.k, self.v = (t.to(device) for t in (q, k, v))
+        self.s = None if s is None else s.to(device)
+        self.out = torch.empty_like(self.q)
+        self.lse = torch.empty(w.B, w.Hq, w.Sq, dtype=torch.float32, device=device)
+        fa.ensure_workspace(self.q.device, fa.fa_fwd_workspace_bytes(w.B, w.Sq, w.Sk, w.Hq, w.Hkv, w.D, w.causal))
+        self.args = (self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(), self.out.data_ptr(),
+                     self.lse.data_ptr(), w.B, w.Sq, w.Sk, w.Hq, w.Hkv, w.D, int(w.causal),
+                     0 if self.s is None else self.s.data_ptr(), w.scale)
+
+    def step(self, stream_handle):
+        rc = self.fa.fa_fwd(*self.args, stream_handle)
+        if rc != self.fa.FA_OK:
+            raise self.fa.FAError(rc, "fa_fwd")
+
+
+def time_graph(fn_launch, steps, warmup, device):
+    """Capture `steps` launches in one graph; time one replay.  Returns
+    (wall seconds between the two synchronisations, event seconds)."""
+    import torch
+
+    stream = torch.cuda.Stream(device=device)
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            fn_launch(stream.cuda_stream)
+    stream.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for _ in range(steps):
+            fn_launch(torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    graph.replay()  # first replay uploads the graph; not timed
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    cur = torch.cuda.current_stream(device)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(cur)
+    graph.replay()  # replays on the current stream
+    e1.record(cur)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, e0.elapsed_time(e1) * 1e-3
+
+
+def dispatch_floor_us(device, steps=200):
+    """Per-launch time of a one-element fill kernel in the same graph setup."""
+    import torch
+
+    x = torch.zeros(1, device=device)
+    _, ev = time_graph(lambda h: x.fill_(1.0), steps, 10, device)
+    return ev / steps * 1e6
+
+
+def cpu_baseline(w, budget_s=10.0, max_runs=50):
+    """The fp64 oracle as it stands, repeated on the full workload until
+    `budget_s` seconds of host time are spent (at least one run)."""
+    import numpy as np
+    from attention_forward_amd.workloads import make_inputs
+    from oracle import attention_ref
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # threadpoolctl missing: report the affinity count
+        threads = len(os.sched_getaffinity(0))
+    q, k, v, s = make_inputs(w.name)
+    q64, k64, v64 = (t.float().numpy().astype(np.float64) for t in (q, k, v))
+    sn = None if s is None else s.numpy()
+    flops, _ = algorithmic(w)
+    runs, t0 = 0, time.perf_counter()
+    while True:
+        attention_ref(q64, k64, v64, causal=w.causal, seqused_k=sn, scale=w.scale)
+        runs += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or runs >= max_runs:
+            break
+    return {"value": round(flops * runs / el / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "sample": f"{runs} full fp64 oracle run(s) of {w.name} in {el:.1f} s",
+            "ms_per_call": round(el / runs * 1e3, 2)}
+
+
+def measure(w, steps, warmup, device):
+    r = Runner(w, device)
+    wall, ev = time_graph(r.step, steps, warmup, device)
+    flops, nbytes = algorithmic(w)
+    return r, wall, ev, flops, nbytes
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-all", action="store_true", help="skip the per-workload table")
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    a = ap.parse_args(argv)
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {a.gpus} is not supported (this library has no "
+              "multi-GPU path; run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+    from attention_forward_amd.workloads import WORKLOADS, WORKLOAD_ORDER
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    device = torch.device("cuda:0")
+    w = WORKLOADS[a.workload]
+    r, wall, ev, flops, nbytes = measure(w, a.steps, a.warmup, device)
+    sec_launch = ev / a.steps
+    bound = binding_roofline(flops, nbytes)
+    traffic = load_traffic(w.name)
+    line = {
+        "metric": METRIC,
+        "value": round(flops * a.steps / wall / 1e12, 4),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(wall / a.steps * 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Sq": w.Sq, "Sk": w.Sk, "seqused_k": w.n_valid,
+                   "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "causal": w.causal, "parallelism": "none (1 GPU)"},
+        "us_per_call": round(sec_launch * 1e6, 3),
+        "roofline": roofline_entry(bound, flops, nbytes, sec_launch, traffic),
+        "algorithmic": {"flops_per_call": flops, "bytes_per_call": nbytes},
+        "kernel_sha": kernel_sha(),
+        "device": torch.cuda.get_device_name(device),
+    }
+    line["dispatch_floor_us"] = round(dispatch_floor_us(device), 3)
+    if not a.no_all:
+        table = {}
+        for name in WORKLOAD_ORDER:
+            wx = WORKLOADS[name]
+            steps = max(50, min(a.steps, 400))
+            _, wl, evx, fx, bx = measure(wx, steps, 5, device)
+            s = evx / steps
+            bnd = binding_roofline(fx, bx)
+            re = roofline_entry(bnd, fx, bx, s)
+            table[name] = {"us_per_call": round(s * 1e6, 3), "tflops": round(fx / s / 1e12, 3),
+                           "bound": bnd, "frac": re["frac"], "achieved": re["achieved"], "unit": re["unit"]}
+        line["all_workloads"] = table
+    if not a.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, budget_s=a.cpu_budget)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,107 @@
+/* Fused attention forward for AMD Instinct MI355X (gfx950): C ABI.
+ *
+ *   out = softmax(scale * Q K^T + mask) V,   lse = log sum exp(scale * Q K^T + mask)
+ *
+ * The operation is the forward of FlashAttention-style attention as the
+ * "flashrt/fa4-cute-runtime" card describes it: section "Functions" (the
+ * forward returns the output together with the per-row log-sum-exp; an
+ * allocation-free entry point writes into caller-owned output for graph
+ * capture), the padded fixed-shape example (a device-resident int32
+ * seqused_k and grouped-query head packing), and the closing section on the
+ * (batch, sequence, heads, head_dim) layout and the qualified D72 MHA and
+ * D256 8-Q/1-KV-head profiles.  Masked keys contribute exactly zero
+ * probability, as in the seqused attention passage of
+ * "pi05_thor_decoder_fp4_e2e.md", section "Fused GeGLU FFN in the Decoder".
+ *
+ * Conventions shared by every entry point:
+ *   - Every pointer argument named q, k, v, out, lse, seqused_k, dev_ptr is a
+ *     DEVICE pointer.  The library never dereferences one on the host, never
+ *     allocates, never synchronises, and never copies between host and
+ *     device, so fa_fwd can be captured into a HIP graph.
+ *   - All memory is owned by the caller.
+ *   - Errors are returned as FA_* codes before any device work is queued;
+ *     nothing is launched when a check fails.  Faults inside a kernel
+ *     surface at the caller's next synchronisation, as with any HIP launch.
+ *   - There is no fallback: an unsupported input is an error, never routed
+ *     to another implementation.
+ */
+#ifndef FA_MI355X_FA_H
+#define FA_MI355X_FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_ABI_VERSION 1
+
+/* Status codes. */
+enum {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,        /* a required pointer is NULL */
+  FA_ERR_SHAPE = 2,       /* a size is < 1, Hq % Hkv != 0, or a size overflows 32-bit indexing */
+  FA_ERR_UNSUPPORTED = 3, /* D not in {64, 72, 256}; causal with Sq != Sk or with seqused_k */
+  FA_ERR_ALIGN = 4,       /* q, k, v, out not 16-byte aligned; lse or seqused_k not 4-byte aligned */
+  FA_ERR_SCALE = 5,       /* scale not finite or not > 0 */
+  FA_ERR_WORKSPACE = 6,   /* the split-KV path needs a workspace that is missing or too small */
+  FA_ERR_LAUNCH = 7,      /* the HIP runtime rejected a kernel launch */
+  FA_ERR_ALIAS = 8        /* out overlaps q, k or v, or lse overlaps one of them */
+};
+
+/* fa_fwd: one attention forward pass.
+ *
+ *   q          [B, Sq, Hq, D]  bf16, contiguous (head_dim fastest)
+ *   k, v       [B, Sk, Hkv, D] bf16, contiguous
+ *   out        [B, Sq, Hq, D]  bf16, written (round to nearest even)
+ *   lse        [B, Hq, Sq]     fp32, written (natural log, scale included),
+ *                              or NULL to skip it
+ *   seqused_k  NULL (all Sk keys valid) or int32[B] on the device: keys
+ *              j >= seqused_k[b] of batch b are neither read nor attended.
+ *              Values are clamped to [0, Sk] on the device.  A row with no
+ *              attended key gets out = 0 and lse = -inf.
+ *   causal     0 or 1.  With 1, query i attends key j only when j <= i; this
+ *              requires Sq == Sk and seqused_k == NULL.
+ *   scale      softmax temperature applied to q.k (finite, > 0), passed as
+ *              float; use 1/sqrt(D) for the usual scaling.
+ *   Hq % Hkv == 0; query head h reads K/V head h / (Hq / Hkv).
+ *   D is 64, 72 or 256.
+ *   stream     HIP stream for the launch (NULL = default stream).
+ *
+ * Some shapes (few packed query rows, long key buffers) take a split-KV
+ * path that needs a workspace registered with fa_set_workspace() on the
+ * current device; fa_fwd_workspace_bytes() says how many bytes (0 when the
+ * single-pass path is used).  Calls that share one workspace must not run
+ * concurrently (one stream at a time per device).
+ *
+ * Returns FA_OK after queueing the work, or an FA_ERR_* code (nothing queued).
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+           int B, int Sq, int Sk, int Hq, int Hkv, int D, int causal,
+           const int32_t* seqused_k, float scale, hipStream_t stream);
+
+/* Bytes of workspace fa_fwd needs for this shape (0: none).  Pure host
+ * arithmetic; returns 0 for invalid shapes as well. */
+size_t fa_fwd_workspace_bytes(int B, int Sq, int Sk, int Hq, int Hkv, int D, int causal);
+
+/* Registers a caller-owned device buffer as the split-KV workspace of the
+ * current HIP device (replacing any earlier one; NULL/0 unregisters).  The
+ * buffer needs no initialisation and must outlive every fa_fwd call queued
+ * with it.  Not thread-safe against concurrent fa_fwd calls.
+ * Returns FA_OK, or FA_ERR_NULL for a NULL pointer with bytes > 0. */
+int fa_set_workspace(void* dev_ptr, size_t bytes);
+
+/* Static, NUL-terminated description of a status code. */
+const char* fa_status_string(int code);
+
+/* FA_ABI_VERSION of the built library. */
+int fa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_FA_H */
