@@ -11,6 +11,9 @@ from .fa import (  # noqa: F401
     attention,
     fa_abi_version,
     fa_fwd,
+    fa_fwd_plan,
+    fa_fwd_variant,
+    fa_fwd_variant_workspace_bytes,
     fa_fwd_workspace_bytes,
     fa_set_workspace,
     fa_status_string,
@@ -23,6 +26,9 @@ __all__ = [
     "attention",
     "fa_abi_version",
     "fa_fwd",
+    "fa_fwd_plan",
+    "fa_fwd_variant",
+    "fa_fwd_variant_workspace_bytes",
     "fa_fwd_workspace_bytes",
     "fa_set_workspace",
     "fa_status_string",

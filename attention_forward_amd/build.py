@@ -29,6 +29,9 @@ HIPCC_FLAGS = [
     "-shared",
     "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs: the softmax rescales O in place every few
+    # tiles, which costs two extra moves per element when O lives in AGPRs.
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"),
 ]
 

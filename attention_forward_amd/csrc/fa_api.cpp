@@ -1,18 +1,20 @@
 // C ABI of the fused attention forward library (declared in include/fa.h).
 //
-// This file holds the host side only: argument checks, the choice between
-// the single-pass and the split-KV kernels, the per-device workspace
-// registry, and the launch.  It never touches device memory: seqused_k is
-// read only by the kernels.  Checks run before any HIP call, so every error
-// path works without a GPU (the failure convention of the pages: explicit
-// errors, never an implicit fallback -- "pi05_thor_decoder_fp4_e2e.md",
-// section "Implemented Path"; probe before capture -- "GROOT N1.7 update",
-// section "Shared-code changes").
+// This file holds the host side only: argument checks, the choice of kernel
+// variant (rows per wave, waves per workgroup, key tile, key split), the
+// per-device workspace registry, and the launch.  It never touches device
+// memory: seqused_k is read only by the kernels.  Checks run before any HIP
+// call, so every error path works without a GPU (the failure convention of
+// the pages: explicit errors, never an implicit fallback --
+// "pi05_thor_decoder_fp4_e2e.md", section "Implemented Path"; fail before
+// capture, naming the cause -- "GROOT N1.7 update", section "Shared-code
+// changes").
 
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "../../include/fa.h"
@@ -21,8 +23,7 @@
 namespace {
 
 constexpr int kMaxDevices = 64;
-constexpr int kSplitMinWorkgroups = 64;  // below this many single-pass workgroups, split the keys
-constexpr int kSplitMinKeys = 256;       // ... but only when the key buffer is longer than this
+constexpr long long kTargetWorkgroups = 256;  // one per compute unit on MI355X
 
 struct Workspace {
   void* ptr = nullptr;
@@ -33,32 +34,71 @@ std::mutex g_ws_mu;
 
 bool supported_d(int D) { return D == 64 || D == 72 || D == 256; }
 
+long long cdiv(long long a, long long b) { return (a + b - 1) / b; }
+
 struct Plan {
-  fa::LaunchPlan launch;
+  fa::LaunchPlan launch{};
   int Mp = 0;
   int kps = 0;
-  size_t ws_bytes = 0;
-  size_t ws_o_bytes = 0;
+  int nrb = 0;
+  int zmax = 0;
+  size_t ws_o_bytes = 0, ws_ml_bytes = 0, ws_bytes = 0;
 };
 
-// Shape-only planning: the same inputs always give the same kernel, tile and
-// split, independent of the device-side seqused_k values.
-Plan make_plan(int B, int Sq, int Sk, int Hq, int Hkv, int D, int causal) {
-  Plan pl;
+int rows_per_block(const fa::LaunchPlan& l) { return l.nw * 16 * l.qt; }
+
+// Fills in the derived fields (row blocks, split count, workspace layout) of
+// a plan whose variant and keys-per-split are set.  kps == 0: no split.
+void finish_plan(Plan& pl, int B, int Sq, int Sk, int Hq, int Hkv, int causal) {
   const int g = Hq / Hkv;
   pl.Mp = Sq * g;
-  pl.launch.D = D;
+  const int rows = rows_per_block(pl.launch);
+  pl.nrb = (int)cdiv(pl.Mp, rows);
   pl.launch.causal = causal != 0;
+  pl.launch.split = pl.kps > 0;
   pl.launch.nsplit = 0;
-  const long long rows_wg = fa::plan_rows_per_wg(D);
-  const long long wgs = (pl.Mp + rows_wg - 1) / rows_wg * (long long)B * Hkv;
-  if (!causal && wgs < kSplitMinWorkgroups && Sk > kSplitMinKeys) {
-    pl.kps = fa::plan_block_keys(D);
-    pl.launch.nsplit = (Sk + pl.kps - 1) / pl.kps;
-    const size_t rows = (size_t)pl.launch.nsplit * B * Hkv * pl.Mp;
-    pl.ws_o_bytes = (rows * D * sizeof(float) + 255) / 256 * 256;
-    pl.ws_bytes = pl.ws_o_bytes + rows * 2 * sizeof(float);
+  pl.zmax = 0;
+  pl.ws_o_bytes = pl.ws_ml_bytes = pl.ws_bytes = 0;
+  if (!pl.launch.split) return;
+  if (causal) {
+    const long long kmax_last = (std::min((long long)pl.nrb * rows, (long long)pl.Mp) - 1) / g + 1;
+    pl.zmax = (int)cdiv(kmax_last, pl.kps);
+  } else {
+    pl.launch.nsplit = (int)cdiv(Sk, pl.kps);
+    pl.zmax = pl.launch.nsplit;
   }
+  const size_t prow = (size_t)B * Hkv * pl.nrb * pl.zmax * rows;
+  // Layout: the partial O rows, then the (m, l) pairs.
+  pl.ws_o_bytes = (prow * pl.launch.D * sizeof(float) + 255) / 256 * 256;
+  pl.ws_ml_bytes = (prow * 2 * sizeof(float) + 255) / 256 * 256;
+  pl.ws_bytes = pl.ws_o_bytes + pl.ws_ml_bytes;
+}
+
+// Default variant for a shape: a function of the shape only (never of the
+// seqused_k values), so equal shapes always run the same kernel.  One wave
+// per 16 packed rows.  When the single-pass grid is at most half the compute
+// units, the key range is split into fixed-size ranges, merged afterwards by
+// the combine kernel.  The range size depends on the grid size only, not on
+// the key buffer length, so a padded buffer and the same keys without the
+// padding are split at the same boundaries (the extra ranges of the padded
+// one are empty and skipped by the merge): their results are bit-identical.
+Plan default_plan(int B, int Sq, int Sk, int Hq, int Hkv, int D, int causal) {
+  Plan pl;
+  pl.launch.D = D;
+  const long long BH = (long long)B * Hkv;
+  const long long Mp = (long long)Sq * (Hq / Hkv);
+  pl.launch.qt = 1;
+  pl.launch.nw = 4;
+  pl.launch.bn = D == 256 ? 32 : 64;
+  pl.launch.nst = 2;
+  const int rows = rows_per_block(pl.launch);
+  const long long base = cdiv(Mp, rows) * BH;
+  pl.kps = 0;
+  if (!causal && base <= kTargetWorkgroups / 2) {
+    const int kps = base <= 32 ? 128 : (base <= 64 ? 256 : 512);
+    if (Sk > kps) pl.kps = kps;
+  }
+  finish_plan(pl, B, Sq, Sk, Hq, Hkv, causal);
   return pl;
 }
 
@@ -78,49 +118,13 @@ int check_shape(int B, int Sq, int Sk, int Hq, int Hkv, int D, int causal) {
   const long long pn = (long long)Sq * (Hq / Hkv);
   if (qn > INT32_MAX || kn > INT32_MAX || pn > INT32_MAX / 2) return FA_ERR_SHAPE;
   if ((long long)B * Hkv > 65535) return FA_ERR_SHAPE;  // grid.y limit
+  if ((long long)Sk * Hkv * D * 2 >= (1ll << 31)) return FA_ERR_SHAPE;  // K/V bytes per batch entry (32-bit offsets)
   if (!supported_d(D)) return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-int fa_abi_version(void) { return FA_ABI_VERSION; }
-
-const char* fa_status_string(int code) {
-  switch (code) {
-    case FA_OK: return "FA_OK: success";
-    case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
-    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: invalid sizes (need all >= 1, Hq % Hkv == 0, 32-bit element counts)";
-    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: unsupported head_dim (64, 72, 256) or causal with Sq != Sk or with seqused_k";
-    case FA_ERR_ALIGN: return "FA_ERR_ALIGN: q/k/v/out must be 16-byte aligned, lse/seqused_k 4-byte aligned";
-    case FA_ERR_SCALE: return "FA_ERR_SCALE: scale must be finite and > 0";
-    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: split-KV path needs a registered workspace of fa_fwd_workspace_bytes() bytes";
-    case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: the HIP runtime reported an error";
-    case FA_ERR_ALIAS: return "FA_ERR_ALIAS: out or lse overlaps an input";
-    default: return "FA_ERR_UNKNOWN: unknown status code";
-  }
-}
-
-size_t fa_fwd_workspace_bytes(int B, int Sq, int Sk, int Hq, int Hkv, int D, int causal) {
-  if (check_shape(B, Sq, Sk, Hq, Hkv, D, causal) != FA_OK) return 0;
-  return make_plan(B, Sq, Sk, Hq, Hkv, D, causal).ws_bytes;
-}
-
-int fa_set_workspace(void* dev_ptr, size_t bytes) {
-  if (dev_ptr == nullptr && bytes > 0) return FA_ERR_NULL;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FA_ERR_LAUNCH;
-  std::lock_guard<std::mutex> lock(g_ws_mu);
-  g_ws[dev].ptr = dev_ptr;
-  g_ws[dev].bytes = dev_ptr ? bytes : 0;
-  return FA_OK;
-}
-
-int fa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
-           int B, int Sq, int Sk, int Hq, int Hkv, int D, int causal,
-           const int32_t* seqused_k, float scale, hipStream_t stream) {
+int check_args(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Sq, int Sk,
+               int Hq, int Hkv, int D, int causal, const int32_t* seqused_k, float scale) {
   if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return FA_ERR_NULL;
   int rc = check_shape(B, Sq, Sk, Hq, Hkv, D, causal);
   if (rc != FA_OK) return rc;
@@ -137,8 +141,27 @@ int fa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
         overlap(lse, lb, out, qb))
       return FA_ERR_ALIAS;
   }
+  return FA_OK;
+}
 
-  const Plan pl = make_plan(B, Sq, Sk, Hq, Hkv, D, causal);
+// Variant given by the caller: checked against the compiled set.
+int variant_plan(Plan& pl, int B, int Sq, int Sk, int Hq, int Hkv, int D, int causal, int qt, int nw, int bn,
+                 int nst, int kps) {
+  if (!fa::variant_exists(D, qt, nw, bn, nst)) return FA_ERR_UNSUPPORTED;
+  if (kps < 0 || (kps > 0 && kps % bn != 0)) return FA_ERR_UNSUPPORTED;
+  pl.launch.D = D;
+  pl.launch.qt = qt;
+  pl.launch.nw = nw;
+  pl.launch.bn = bn;
+  pl.launch.nst = nst;
+  pl.kps = kps;
+  finish_plan(pl, B, Sq, Sk, Hq, Hkv, causal);
+  return FA_OK;
+}
+
+int run(const Plan& pl, const void* q, const void* k, const void* v, void* out, float* lse, int B, int Sq,
+        int Sk, int Hq, int Hkv, int causal, const int32_t* seqused_k, float scale, hipStream_t stream) {
+  (void)causal;
   fa::FwdParams p{};
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k);
@@ -154,9 +177,10 @@ int fa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
   p.g = Hq / Hkv;
   p.Mp = pl.Mp;
   p.kps = pl.kps;
+  p.nrb = pl.nrb;
+  p.zmax = pl.zmax;
   p.scale_log2 = scale * 1.4426950408889634f;
-
-  if (pl.launch.nsplit > 0) {
+  if (pl.launch.split) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FA_ERR_LAUNCH;
     Workspace ws;
@@ -165,12 +189,91 @@ int fa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
       ws = g_ws[dev];
     }
     if (ws.ptr == nullptr || ws.bytes < pl.ws_bytes || !aligned(ws.ptr, 256)) return FA_ERR_WORKSPACE;
-    p.ws_o = static_cast<float*>(ws.ptr);
-    p.ws_ml = reinterpret_cast<float*>(static_cast<char*>(ws.ptr) + pl.ws_o_bytes);
+    char* base = static_cast<char*>(ws.ptr);
+    p.ws_o = reinterpret_cast<float*>(base);
+    p.ws_ml = reinterpret_cast<float*>(base + pl.ws_o_bytes);
   }
-
   const hipError_t e = fa::launch_fwd(p, pl.launch, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+size_t padded_ws_bytes(const Plan& pl) { return pl.launch.split ? pl.ws_bytes : 0; }
+
+}  // namespace
+
+extern "C" {
+
+int fa_abi_version(void) { return FA_ABI_VERSION; }
+
+const char* fa_status_string(int code) {
+  switch (code) {
+    case FA_OK: return "FA_OK: success";
+    case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
+    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: invalid sizes (need all >= 1, Hq % Hkv == 0, 32-bit element counts)";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: unsupported head_dim (64, 72, 256), kernel variant, or causal with Sq != Sk or with seqused_k";
+    case FA_ERR_ALIGN: return "FA_ERR_ALIGN: q/k/v/out must be 16-byte aligned, lse/seqused_k 4-byte aligned";
+    case FA_ERR_SCALE: return "FA_ERR_SCALE: scale must be finite and > 0";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: split-KV path needs a registered workspace of fa_fwd_workspace_bytes() bytes";
+    case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: the HIP runtime reported an error";
+    case FA_ERR_ALIAS: return "FA_ERR_ALIAS: out or lse overlaps an input";
+    default: return "FA_ERR_UNKNOWN: unknown status code";
+  }
+}
+
+size_t fa_fwd_workspace_bytes(int B, int Sq, int Sk, int Hq, int Hkv, int D, int causal) {
+  if (check_shape(B, Sq, Sk, Hq, Hkv, D, causal) != FA_OK) return 0;
+  return padded_ws_bytes(default_plan(B, Sq, Sk, Hq, Hkv, D, causal));
+}
+
+size_t fa_fwd_variant_workspace_bytes(int B, int Sq, int Sk, int Hq, int Hkv, int D, int causal, int qt, int nw,
+                                      int bn, int nst, int kps) {
+  if (check_shape(B, Sq, Sk, Hq, Hkv, D, causal) != FA_OK) return 0;
+  Plan pl;
+  if (variant_plan(pl, B, Sq, Sk, Hq, Hkv, D, causal, qt, nw, bn, nst, kps) != FA_OK) return 0;
+  return padded_ws_bytes(pl);
+}
+
+int fa_set_workspace(void* dev_ptr, size_t bytes) {
+  if (dev_ptr == nullptr && bytes > 0) return FA_ERR_NULL;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FA_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  g_ws[dev].ptr = dev_ptr;
+  g_ws[dev].bytes = dev_ptr ? bytes : 0;
+  return FA_OK;
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Sq, int Sk, int Hq,
+           int Hkv, int D, int causal, const int32_t* seqused_k, float scale, hipStream_t stream) {
+  int rc = check_args(q, k, v, out, lse, B, Sq, Sk, Hq, Hkv, D, causal, seqused_k, scale);
+  if (rc != FA_OK) return rc;
+  const Plan pl = default_plan(B, Sq, Sk, Hq, Hkv, D, causal);
+  return run(pl, q, k, v, out, lse, B, Sq, Sk, Hq, Hkv, causal, seqused_k, scale, stream);
+}
+
+int fa_fwd_variant(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Sq, int Sk,
+                   int Hq, int Hkv, int D, int causal, const int32_t* seqused_k, float scale, int qt, int nw,
+                   int bn, int nst, int kps, hipStream_t stream) {
+  int rc = check_args(q, k, v, out, lse, B, Sq, Sk, Hq, Hkv, D, causal, seqused_k, scale);
+  if (rc != FA_OK) return rc;
+  Plan pl;
+  rc = variant_plan(pl, B, Sq, Sk, Hq, Hkv, D, causal, qt, nw, bn, nst, kps);
+  if (rc != FA_OK) return rc;
+  return run(pl, q, k, v, out, lse, B, Sq, Sk, Hq, Hkv, causal, seqused_k, scale, stream);
+}
+
+int fa_fwd_plan(int B, int Sq, int Sk, int Hq, int Hkv, int D, int causal, int* qt, int* nw, int* bn, int* nst,
+                int* kps) {
+  int rc = check_shape(B, Sq, Sk, Hq, Hkv, D, causal);
+  if (rc != FA_OK) return rc;
+  if (qt == nullptr || nw == nullptr || bn == nullptr || nst == nullptr || kps == nullptr) return FA_ERR_NULL;
+  const Plan pl = default_plan(B, Sq, Sk, Hq, Hkv, D, causal);
+  *qt = pl.launch.qt;
+  *nw = pl.launch.nw;
+  *bn = pl.launch.bn;
+  *nst = pl.launch.nst;
+  *kps = pl.kps;
+  return FA_OK;
 }
 
 }  // extern "C"

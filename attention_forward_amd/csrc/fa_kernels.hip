@@ -13,44 +13,64 @@
 //    folded into the row dimension.  Packed row r of (batch b, kv head hk)
 //    is query position r / g of head hk*g + r % g, so one K/V tile staged in
 //    LDS serves every head of the group.
-//  * Each wave owns 16*QT packed rows.  The contraction is written
-//    transposed, S^T = K * Q^T and O^T = V^T * P^T, with the bf16 MFMA
-//    v_mfma_f32_16x16x32_bf16.  In the 16x16 accumulator layout lane l holds
-//    column l%16, so every lane owns one query row: the softmax statistics
-//    live in that lane, the O^T rescale needs no data movement, and the
-//    S^T accumulator is already the P^T operand of the second MFMA.
-//  * K tiles sit row-major in LDS (padded rows, conflict-free 16-byte
-//    reads).  V tiles are written transposed (d-major), with keys permuted
-//    inside each 32-key block to match the order P^T comes out of the S^T
-//    accumulators, and an XOR swizzle of 16-byte chunks per row.
-//  * Online softmax in base 2: t = s*scale*log2(e); running max m and sum l
-//    per row; O^T is rescaled by exp2(m_old - m_new) per K/V tile.
-//  * Masking touches only the tile that crosses the valid length and the
-//    causal diagonal tiles; keys at or past the valid length are never
-//    loaded and their V rows in LDS are zero, so padding (even inf/nan)
-//    cannot reach an accumulator.
-//  * Split-KV variant: blockIdx.z picks a key range; the partial (m, l,
-//    O/l) goes to a workspace and a second kernel merges the splits in
-//    fixed order (deterministic; no float atomics).
+//  * Each wave owns 16*QT packed rows; all waves share the K/V tiles.  The
+//    contractions are written transposed, S^T = K * Q^T and O^T = V^T * P^T,
+//    on v_mfma_f32_16x16x32_bf16.  In the 16x16 accumulator layout lane l
+//    holds column l%16, so every lane owns one query row: its softmax
+//    statistics stay in the lane, the O^T rescale needs no data movement,
+//    and the S^T accumulator is already the P^T operand of the second MFMA.
+//  * K and V tiles are stored row-major in LDS with padded row strides
+//    (K rows 16 bytes apart modulo 128, V rows 32 bytes apart modulo 128)
+//    so that the fragment reads are free of bank conflicts and every read
+//    address is one per-lane base plus a compile-time offset.  The tiles are
+//    filled by buffer loads that write LDS directly (no VGPR staging); rows
+//    at or past the end of the key range fall outside the buffer range and
+//    arrive as zeros, so padding keys are never read from memory.  The V^T
+//    operand is read with ds_read_b64_tr_b16, which transposes 16-bit data
+//    on the way out of LDS.
+//  * A ring of NST K/V stages: the loads of the next NST-1 tiles are in
+//    flight while one tile is computed.
+//  * Online softmax in base 2: t = s*scale*log2(e), running max m and sum
+//    l per row, row reductions across the four 16-lane rows with
+//    v_permlane16/32_swap.  The rescale of O is lazy: the running max is
+//    only moved (and O, l rescaled) when a row's max grows by more than 2^8,
+//    otherwise exp2 is taken against the stale max (values stay <= 256).
+//  * Masking touches only the tile that crosses the end of the key range
+//    and the causal diagonal tiles.
+//  * Split-KV: several workgroups share one block of rows and each takes a
+//    key range.  Each writes its partial (O/l, m, l) to the workspace; a
+//    second, fully parallel kernel on the same stream merges the partials of
+//    every row in fixed split order (deterministic, no float atomics).
+//  * Causal: row blocks are dispatched heaviest first; with splitting, the
+//    key range [0, last position of the block] is cut into fixed chunks.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <algorithm>
 
 #include "fa_launch.h"
 
 namespace fa {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 static constexpr float kLn2 = 0.6931471805599453f;
+static constexpr float kRescaleThreshold = 8.0f;  // log2 units: rescale when the max grows by > 2^8
+constexpr int kRawBufferFlags = 0x00020000;       // dword 3 of a raw (untyped) buffer resource on gfx9
+constexpr uint32_t kOutOfRange = 0x80000000u;     // a buffer offset past any range: reads as zero
 
-__device__ __forceinline__ u32x4_t ldg16(const uint16_t* p) {
-  return *reinterpret_cast<const u32x4_t*>(p);
-}
+// s_waitcnt immediate with vmcnt = n and expcnt / lgkmcnt left at their
+// maxima (vmcnt is split over bits 3:0 and 15:14).
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
+__device__ __forceinline__ u32x4_t ldg16(const uint16_t* p) { return *reinterpret_cast<const u32x4_t*>(p); }
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t x) { return __builtin_bit_cast(bf16x8_t, x); }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -59,53 +79,93 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
-__device__ __forceinline__ float wave_max_groups(float x) {
-  // max over lanes l, l^16, l^32, l^48 (the four 16-lane rows holding one column)
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+// x combined over lanes l, l^16, l^32, l^48 (the four 16-lane rows that hold
+// one accumulator column).  permlane32_swap(x, x) gives {x[l & 31], x[l | 32]}
+// per lane, permlane16_swap(x, x) gives {x[l & ~16], x[l | 16]}.
+__device__ __forceinline__ float group_max(float x) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float group_sum(float x) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-__device__ __forceinline__ float wave_sum_groups(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+// One 16-byte copy per lane from a buffer to LDS (buffer_load_dwordx4 with
+// the LDS bit): lane i of the wave writes LDS bytes [lds + 16 i, +16) with
+// the 16 bytes at buffer offset voff, or zeros when that offset is past the
+// buffer's range.  Inline asm so that the compiler adds no waits for
+// it in front of later LDS reads: the main loop waits for these copies
+// itself (s_waitcnt vmcnt and a barrier before a stage is read).  The
+// instruction has no register result; M0 carries the wave-uniform LDS
+// address and is used by nothing else in these kernels.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void copy16_to_lds(u32x4_t rsrc, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "s"(lds)
+               : "memory", "m0");
 }
 
-// Position of key kr (0..BN-1) inside the transposed V row.  Within each
-// 32-key block, slot 8*grp + e holds the key that the S^T accumulators give
-// lane group grp in element e of the P^T operand: e < 4 -> key 4*grp + e of
-// the first 16-key M-tile, e >= 4 -> key 16 + 4*grp + (e - 4) of the second.
-__device__ __forceinline__ int vt_slot(int kr) {
-  const int blk = kr >> 5, kb = kr & 31;
-  const int half = kb >> 4, w = kb & 15;
-  return blk * 32 + (w >> 2) * 8 + (w & 3) + 4 * half;
+// Raw buffer resource (stride 0, byte range `bytes`) for a wave-uniform base
+// address, built in scalar registers.
+__device__ __forceinline__ u32x4_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  return u32x4_t{(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a),
+                 (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu),
+                 (uint32_t)__builtin_amdgcn_readfirstlane(bytes), (uint32_t)kRawBufferFlags};
 }
+#pragma clang diagnostic pop
 
-// XOR swizzle of the 16-byte chunk index inside a transposed-V row.
-template <int BN>
-__device__ __forceinline__ int vt_swz(int d) {
-  constexpr int kChunks = BN / 8;
-  return (d ^ (d >> 3)) & (kChunks - 1);
-}
+constexpr int round_up(int x, int m) { return (x + m - 1) / m * m; }
+// Smallest LDS row stride >= bytes that is 32 modulo 128 (V rows).
+constexpr int v_stride(int bytes) { return (bytes % 128 == 32) ? bytes : v_stride(bytes + 16); }
 
-template <int D, int QT, int NW, int BN, bool CAUSAL, bool SPLIT>
-__global__ void __launch_bounds__(NW * 64)
+// Compile-time geometry of one kernel variant.
+template <int D, int QT, int NW, int BN>
+struct Geo {
+  static constexpr int CPR = D / 8;              // 16-byte chunks per K/V row
+  static constexpr int ROWB = D * 2;             // bytes per K/V row
+  // LDS row strides: K rows 16 bytes apart modulo 128 (16 rows read with
+  // 16-byte loads hit distinct banks), V rows 32 bytes apart modulo 128 (the
+  // transpose reads take 32 contiguous bytes from each of 4 rows).
+  static constexpr int KSTR = (ROWB % 128 == 0) ? ROWB + 16 : ROWB;
+  static constexpr int VSTR = v_stride(ROWB);
+  static constexpr int NT = NW * 64;             // threads
+  static constexpr int K_SLOTS = round_up(BN * (KSTR / 16), 64);  // 16-byte slots per K tile
+  static constexpr int V_SLOTS = round_up(BN * (VSTR / 16), 64);
+  static constexpr int LPT_K = (K_SLOTS + NT - 1) / NT;  // copies per thread per K tile
+  static constexpr int LPT_V = (V_SLOTS + NT - 1) / NT;
+  static constexpr int LPT = LPT_K + LPT_V;
+  static constexpr bool TRASH = (K_SLOTS % NT) != 0 || (V_SLOTS % NT) != 0;
+  static constexpr int K_B = K_SLOTS * 16;
+  static constexpr int STAGE_B = K_B + V_SLOTS * 16;  // K tile then V tile
+  static constexpr int KC = (D + 31) / 32;       // K steps of S^T = K Q^T
+  static constexpr int DT = (D + 15) / 16;       // 16-row tiles of O^T
+  static constexpr int MT = BN / 16;             // 16-key tiles of S^T
+  static constexpr int KVC = BN / 32;            // 32-key K steps of O^T
+  static constexpr int ROWS_WG = NW * 16 * QT;
+  static_assert(D % 8 == 0, "head dim must be a multiple of 8");
+  static_assert(BN % 32 == 0, "key tile must be a multiple of 32");
+  static_assert(DT * 16 * 2 <= VSTR, "V fragment reads stay inside a padded row");
+};
+
+struct RowBlock {
+  int rb;      // row block index
+  int z;       // key chunk (split) index
+  int kbeg, kend;
+};
+
+template <int D, int QT, int NW, int BN, int NST, bool CAUSAL, bool SPLIT>
+__global__ void __launch_bounds__(NW * 64, 1)
 fwd_kernel(const FwdParams p) {
-  constexpr int DP = (D + 31) / 32 * 32;  // head dim padded to the MFMA K step
-  constexpr int KC = DP / 32;             // K steps of S^T = K * Q^T
-  constexpr int DT = (D + 15) / 16;       // 16-row tiles of O^T
-  constexpr int KSTR = DP + 8;            // K row stride in LDS (elements)
-  constexpr int VSTR = BN;                // transposed-V row stride (elements)
-  constexpr int MT = BN / 16;             // 16-key M tiles of S^T
-  constexpr int KVC = BN / 32;            // 32-key K steps of O^T
-  constexpr int CPR = D / 8;              // 16-byte chunks per K/V row
-  constexpr int NT = NW * 64;
-  constexpr int ROWS_WG = NW * 16 * QT;
-  static_assert(D % 8 == 0 && BN % 32 == 0, "tile shape");
-
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BN * KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[DT * 16 * VSTR];
+  using G = Geo<D, QT, NW, BN>;
+  static_assert(NST >= 2, "at least double buffering");
+  __shared__ __attribute__((aligned(16))) uint8_t stage[NST * G::STAGE_B];
+  __shared__ __attribute__((aligned(16))) uint8_t trash[G::TRASH ? NW * 1024 : 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -113,58 +173,48 @@ fwd_kernel(const FwdParams p) {
   const int bh = blockIdx.y;
   const int b = bh / p.Hkv, hk = bh - b * p.Hkv;
   const int g = p.g;
-  const int row0 = blockIdx.x * ROWS_WG;
-  const int rw0 = row0 + wave * 16 * QT;
 
   int nvalid = p.Sk;
   if (p.seqused != nullptr) nvalid = min(max(p.seqused[b], 0), p.Sk);
-  int kbeg = 0, kend = nvalid;
-  if constexpr (SPLIT) {
-    kbeg = blockIdx.z * p.kps;
-    kend = min(kbeg + p.kps, nvalid);
-  }
-  if constexpr (CAUSAL) {
-    const int rlast = min(row0 + ROWS_WG, p.Mp) - 1;
-    kend = min(kend, rlast / g + 1);
-  }
+  nvalid = __builtin_amdgcn_readfirstlane(nvalid);  // uniform: keeps the buffer resources in SGPRs
 
-  // Q^T fragments (B operand of S^T): lane (col, grp) holds row rw0+16t+col,
-  // head-dim elements 32c + 8grp .. +7.
-  bf16x8_t qf[QT][KC];
-  int srow[QT];
-#pragma unroll
-  for (int t = 0; t < QT; ++t) {
-    const int r = rw0 + 16 * t + col;
-    const bool ok = r < p.Mp;
-    const int s = ok ? r / g : 0;
-    const int hh = ok ? r - s * g : 0;
-    srow[t] = ok ? s : -1;
-    const uint16_t* qp = p.q + ((size_t)(b * p.Sq + s) * p.Hq + hk * g + hh) * D;
-#pragma unroll
-    for (int c = 0; c < KC; ++c) {
-      const int d0 = 32 * c + 8 * grp;
-      u32x4_t x = {0u, 0u, 0u, 0u};
-      if (ok && d0 < D) x = ldg16(qp + d0);
-      qf[t][c] = as_bf16x8(x);
+  // Which rows and keys this workgroup takes.
+  RowBlock blk;
+  if constexpr (CAUSAL) {
+    // Heaviest row blocks first: walk from the last block down.
+    const int nrb = (p.Mp + G::ROWS_WG - 1) / G::ROWS_WG;
+    int item = blockIdx.x, rb = nrb - 1;
+    for (; rb >= 0; --rb) {
+      const int kmax = (min((rb + 1) * G::ROWS_WG, p.Mp) - 1) / g + 1;
+      const int nz = SPLIT ? (kmax + p.kps - 1) / p.kps : 1;
+      if (item < nz) break;
+      item -= nz;
     }
+    blk.rb = rb;
+    blk.z = item;
+    const int kmax = (min((rb + 1) * G::ROWS_WG, p.Mp) - 1) / g + 1;
+    blk.kbeg = SPLIT ? item * p.kps : 0;
+    blk.kend = SPLIT ? min(blk.kbeg + p.kps, kmax) : kmax;
+    blk.kend = min(blk.kend, nvalid);
+  } else {
+    blk.rb = blockIdx.x;
+    blk.z = SPLIT ? blockIdx.z : 0;
+    blk.kbeg = SPLIT ? blk.z * p.kps : 0;
+    blk.kend = SPLIT ? min(blk.kbeg + p.kps, nvalid) : nvalid;
   }
-  // The wave's smallest and largest query position (causal tile skipping).
+  const int row0 = blk.rb * G::ROWS_WG;
+  const int rw0 = row0 + wave * 16 * QT;
+  const int kbeg = blk.kbeg, kend = blk.kend;
+
+  bf16x8_t qf[QT][G::KC];
+  int srow[QT];
+  const bool wave_active = rw0 < p.Mp;
   const int s_lo = min(rw0, p.Mp - 1) / g;
   const int s_hi = (min(rw0 + 16 * QT, p.Mp) - 1) / g;
-  const bool wave_active = rw0 < p.Mp;
 
-  // Zero the head-dim padding columns of the K tile once (D = 72 -> 96).
-  if constexpr (DP > D) {
-    constexpr int PADC = (DP - D) / 8;
-    for (int i = tid; i < BN * PADC; i += NT) {
-      const int kr = i / PADC, pc = i - kr * PADC;
-      *reinterpret_cast<u32x4_t*>(&Ks[kr * KSTR + D + 8 * pc]) = u32x4_t{0u, 0u, 0u, 0u};
-    }
-  }
-
-  f32x4_t oacc[DT][QT];
+  f32x4_t oacc[G::DT][QT];
 #pragma unroll
-  for (int i = 0; i < DT; ++i)
+  for (int i = 0; i < G::DT; ++i)
 #pragma unroll
     for (int t = 0; t < QT; ++t) oacc[i][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run[QT], l_run[QT];
@@ -174,131 +224,250 @@ fwd_kernel(const FwdParams p) {
     l_run[t] = 0.f;
   }
   const float c2 = p.scale_log2;
+
+  // ---- K/V tile copies.  Buffers start at this (batch, kv head)'s first key
+  // and end after key kend - 1, so every key at or past kend reads as zero.
+  const uint32_t rstride_b = (uint32_t)(p.Hkv * D * 2);  // bytes between consecutive keys
   const size_t kv_base = ((size_t)b * p.Sk * p.Hkv + hk) * D;
-  const size_t kv_rstride = (size_t)p.Hkv * D;
-
-  for (int kt = kbeg; kt < kend; kt += BN) {
-    __syncthreads();  // previous tile fully consumed
-    for (int i = tid; i < BN * CPR; i += NT) {
-      const int kr = i / CPR, ch = i - kr * CPR;
-      const int j = kt + kr;
-      u32x4_t kx = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
-      if (j < kend) {
-        const size_t off = kv_base + (size_t)j * kv_rstride + 8 * ch;
-        kx = ldg16(p.k + off);
-        vx = ldg16(p.v + off);
-      }
-      *reinterpret_cast<u32x4_t*>(&Ks[kr * KSTR + 8 * ch]) = kx;
-      const int slot = vt_slot(kr);
+  const uint32_t kv_range = (uint32_t)kend * rstride_b;
+  const u32x4_t rk = make_rsrc(p.k + kv_base, kv_range);
+  const u32x4_t rv = make_rsrc(p.v + kv_base, kv_range);
+  // Per-thread source offsets of its slots within a tile: slot P holds row
+  // P / (STR/16), chunk P % (STR/16); padding chunks and trash windows read
+  // out of range (zeros, no memory access).
+  uint32_t voff_k[G::LPT_K], voff_v[G::LPT_V];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = 8 * ch + e;
-        const uint32_t word = vx[e >> 1];
-        const uint16_t val = (e & 1) ? (uint16_t)(word >> 16) : (uint16_t)(word & 0xffffu);
-        const int pchunk = (slot >> 3) ^ vt_swz<BN>(d);
-        Vt[d * VSTR + pchunk * 8 + (slot & 7)] = val;
-      }
+  for (int j = 0; j < G::LPT_K; ++j) {
+    const int P = j * G::NT + tid;
+    const int row = P / (G::KSTR / 16), ch = P - row * (G::KSTR / 16);
+    voff_k[j] = (P < G::K_SLOTS && ch < G::CPR) ? row * rstride_b + ch * 16 : kOutOfRange;
+  }
+#pragma unroll
+  for (int j = 0; j < G::LPT_V; ++j) {
+    const int P = j * G::NT + tid;
+    const int row = P / (G::VSTR / 16), ch = P - row * (G::VSTR / 16);
+    voff_v[j] = (P < G::V_SLOTS && ch < G::CPR) ? row * rstride_b + ch * 16 : kOutOfRange;
+  }
+  const uint32_t lds_stage0 = (uint32_t)(uintptr_t)(lds_void_t*)stage;
+  const uint32_t lds_trash = (uint32_t)(uintptr_t)(lds_void_t*)trash + wave * 1024;
+  // The tile's key offset goes into the per-lane offset (not soffset), so
+  // the range check sees the full offset; key bytes per batch and head stay
+  // below 2^31 (checked on the host), so adding it to kOutOfRange cannot wrap.
+  auto issue = [&](int it) __attribute__((always_inline)) {
+    const uint32_t st = lds_stage0 + (it % NST) * G::STAGE_B;
+    const uint32_t toff = (uint32_t)(kbeg + it * BN) * rstride_b;
+#pragma unroll
+    for (int j = 0; j < G::LPT_K; ++j) {
+      const int pbase = j * G::NT + wave * 64;
+      const uint32_t dst = (!G::TRASH || pbase < G::K_SLOTS) ? st + pbase * 16 : lds_trash;
+      copy16_to_lds(rk, voff_k[j] + toff, __builtin_amdgcn_readfirstlane(dst));
     }
-    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < G::LPT_V; ++j) {
+      const int pbase = j * G::NT + wave * 64;
+      const uint32_t dst = (!G::TRASH || pbase < G::V_SLOTS) ? st + G::K_B + pbase * 16 : lds_trash;
+      copy16_to_lds(rv, voff_v[j] + toff, __builtin_amdgcn_readfirstlane(dst));
+    }
+  };
 
-    if (!wave_active) continue;
+  // Per-lane LDS read bases: K fragment (row col of a 16-key tile, chunk
+  // grp of a 32-element step), V transpose read (row 4grp + r, head-dim 4q).
+  const int vr = lane >> 2 & 3, vq = lane & 3;
+  const uint32_t k_lane = col * G::KSTR + grp * 16;
+  const uint32_t v_lane = G::K_B + (4 * grp + vr) * G::VSTR + vq * 8;
+
+  // One K/V tile of the main loop, read from stage `st`.
+  auto compute_tile = [&](const uint8_t* st, int kt) __attribute__((always_inline)) {
+    if (!wave_active) return;
     if constexpr (CAUSAL) {
-      if (kt > s_hi) continue;  // whole tile above the diagonal for this wave
+      if (kt > s_hi) return;  // tile entirely above this wave's diagonal
     }
+    const uint8_t* kb = st + k_lane;
+    const uint8_t* vb = st + v_lane;
+
+    // Fragment loads run a few steps ahead of the MFMAs that use them; the
+    // scheduling barriers keep that order so LDS latency overlaps MFMA work.
+    auto load_k = [&](int c, int mt) __attribute__((always_inline)) -> bf16x8_t {
+      if constexpr (4 * (G::KC - 1) + 3 >= G::CPR) {  // head dim not a multiple of 32 (D = 72)
+        if (4 * c + grp >= G::CPR) return as_bf16x8(u32x4_t{0u, 0u, 0u, 0u});
+      }
+      return as_bf16x8(*reinterpret_cast<const u32x4_t*>(kb + mt * 16 * G::KSTR + c * 64));
+    };
+    // V^T fragment for 32-key step kc and head-dim tile dt.  Lane 16grp+4r+q
+    // of read h points at V row 32kc + 16h + 4grp + r, head-dim 16dt + 4q..+3;
+    // the transpose read hands lane (col, grp) the four keys of that group at
+    // head-dim 16dt + col, i.e. the slots P^T holds in elements 4h .. 4h+3.
+    // Past the head dim (D = 72, dt = 4) the reads land in the row padding.
+    auto load_v = [&](int kc, int dt) __attribute__((always_inline)) -> bf16x8_t {
+      const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vb + (32 * kc) * G::VSTR + dt * 32));
+      const i16x4_t hi =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vb + (32 * kc + 16) * G::VSTR + dt * 32));
+      const u32x4_t vw = {__builtin_bit_cast(u32x2_t, lo)[0], __builtin_bit_cast(u32x2_t, lo)[1],
+                          __builtin_bit_cast(u32x2_t, hi)[0], __builtin_bit_cast(u32x2_t, hi)[1]};
+      return as_bf16x8(vw);
+    };
 
     // S^T = K * Q^T : lane (col, grp) gets query col, keys 16mt + 4grp + r.
-    f32x4_t sacc[MT][QT];
+    constexpr int PFK = G::KC < 3 ? G::KC : 3;
+    f32x4_t sacc[G::MT][QT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
       for (int t = 0; t < QT; ++t) sacc[mt][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    bf16x8_t kf[G::KC][G::MT];
 #pragma unroll
-    for (int c = 0; c < KC; ++c) {
+    for (int c = 0; c < PFK; ++c)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const bf16x8_t kf = as_bf16x8(
-            *reinterpret_cast<const u32x4_t*>(&Ks[(16 * mt + col) * KSTR + 32 * c + 8 * grp]));
+      for (int mt = 0; mt < G::MT; ++mt) kf[c][mt] = load_k(c, mt);
+#pragma unroll
+    for (int c = 0; c < G::KC; ++c) {
+      if (c + PFK < G::KC) {
+#pragma unroll
+        for (int mt = 0; mt < G::MT; ++mt) kf[c + PFK][mt] = load_k(c + PFK, mt);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
         for (int t = 0; t < QT; ++t)
-          sacc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[t][c], sacc[mt][t], 0, 0, 0);
-      }
+          sacc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[c][mt], qf[t][c], sacc[mt][t], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
 
+    // The first V^T fragments go out before the softmax arithmetic.
+    constexpr int NV = G::KVC * G::DT;
+    constexpr int PFV = NV < 4 ? NV : 4;
+    bf16x8_t vf[NV];
+#pragma unroll
+    for (int i = 0; i < PFV; ++i) vf[i] = load_v(i / G::DT, i % G::DT);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // Softmax on the raw scores s (scale > 0, so max commutes with it):
+    // p = exp2(s * scale*log2e - m) in one fma + exp.
     const bool need_mask = (kt + BN > kend) || (CAUSAL && kt + BN - 1 > s_lo);
-    uint32_t pk[KVC][QT][4];
+    uint32_t pk[G::KVC][QT][4];
 #pragma unroll
     for (int t = 0; t < QT; ++t) {
       float mx = -INFINITY;
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+      for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          float x = sacc[mt][t][r] * c2;
+          float x = sacc[mt][t][r];
           if (need_mask) {
             const int key = kt + 16 * mt + 4 * grp + r;
             bool ok = key < kend;
             if constexpr (CAUSAL) ok = ok && key <= srow[t];
             x = ok ? x : -INFINITY;
+            sacc[mt][t][r] = x;
           }
-          sacc[mt][t][r] = x;
           mx = fmaxf(mx, x);
         }
-      mx = wave_max_groups(mx);
+      mx = group_max(mx) * c2;
       const float m_new = fmaxf(m_run[t], mx);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run[t] - m_use);
-      m_run[t] = m_new;
+      if (__ballot(m_new > m_run[t] + kRescaleThreshold) != 0) {
+        const float alpha = __builtin_amdgcn_exp2f(m_run[t] - m_new);  // 0 when m_run = -inf
+        m_run[t] = m_new;
+        l_run[t] *= alpha;
+#pragma unroll
+        for (int i = 0; i < G::DT; ++i) oacc[i][t] *= alpha;
+      }
+      const float m_neg = (m_run[t] == -INFINITY) ? 0.f : -m_run[t];
       float lsum = 0.f;
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+      for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float pv = __builtin_amdgcn_exp2f(sacc[mt][t][r] - m_use);
+          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][t][r], c2, m_neg));
           sacc[mt][t][r] = pv;
           lsum += pv;
         }
-      l_run[t] = l_run[t] * alpha + lsum;
+      l_run[t] += lsum;
 #pragma unroll
-      for (int i = 0; i < DT; ++i) oacc[i][t] *= alpha;
-#pragma unroll
-      for (int kc = 0; kc < KVC; ++kc) {
+      for (int kc = 0; kc < G::KVC; ++kc) {
         pk[kc][t][0] = pack_bf16x2(sacc[2 * kc][t][0], sacc[2 * kc][t][1]);
         pk[kc][t][1] = pack_bf16x2(sacc[2 * kc][t][2], sacc[2 * kc][t][3]);
         pk[kc][t][2] = pack_bf16x2(sacc[2 * kc + 1][t][0], sacc[2 * kc + 1][t][1]);
         pk[kc][t][3] = pack_bf16x2(sacc[2 * kc + 1][t][2], sacc[2 * kc + 1][t][3]);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
 
     // O^T += V^T * P^T : lane (col, grp) gets query col, head-dim 16dt + 4grp + r.
 #pragma unroll
-    for (int kc = 0; kc < KVC; ++kc) {
+    for (int i = 0; i < NV; ++i) {
+      const int kc = i / G::DT, dt = i % G::DT;
+      if (i + PFV < NV) vf[i + PFV] = load_v((i + PFV) / G::DT, (i + PFV) % G::DT);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int d = 16 * dt + col;
-        const int pchunk = (4 * kc + grp) ^ vt_swz<BN>(d);
-        const bf16x8_t vf = as_bf16x8(*reinterpret_cast<const u32x4_t*>(&Vt[d * VSTR + pchunk * 8]));
-#pragma unroll
-        for (int t = 0; t < QT; ++t) {
-          const u32x4_t pw = {pk[kc][t][0], pk[kc][t][1], pk[kc][t][2], pk[kc][t][3]};
-          oacc[dt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, as_bf16x8(pw), oacc[dt][t], 0, 0, 0);
-        }
+      for (int t = 0; t < QT; ++t) {
+        const u32x4_t pw = {pk[kc][t][0], pk[kc][t][1], pk[kc][t][2], pk[kc][t][3]};
+        oacc[dt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[i], as_bf16x8(pw), oacc[dt][t], 0, 0, 0);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
-  }
+  };
 
-  if (!wave_active) return;
+  // Main loop over a ring of NST K/V stages: tile it sits in stage it % NST
+  // and the loads of tiles it+1 .. it+NST-1 are in flight while tile it is
+  // computed.  Each tile costs every thread exactly LPT copies, so waiting
+  // until at most (NST-2)*LPT copies are outstanding means tile it landed.
+  const int ntiles = kend > kbeg ? (kend - kbeg + BN - 1) / BN : 0;
+#pragma unroll
+  for (int it = 0; it < NST - 1; ++it)
+    if (it < ntiles) issue(it);
 
+  // Q^T fragments (B operand of S^T): lane (col, grp) holds packed row
+  // rw0 + 16t + col, head-dim elements 32c + 8grp .. +7 (zero past D).
+  // Loaded after the first K/V copies are on their way.
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
-    const float l = wave_sum_groups(l_run[t]);
     const int r = rw0 + 16 * t + col;
-    if (r >= p.Mp) continue;
-    const int s = r / g, hh = r - s * g;
-    const float inv = (l > 0.f) ? 1.0f / l : 0.f;
-    if constexpr (!SPLIT) {
+    const bool ok = r < p.Mp;
+    const int s = ok ? r / g : 0;
+    const int hh = ok ? r - s * g : 0;
+    srow[t] = ok ? s : -1;
+    const uint16_t* qp = p.q + ((size_t)(b * p.Sq + s) * p.Hq + hk * g + hh) * D;
+#pragma unroll
+    for (int c = 0; c < G::KC; ++c) {
+      const int d0 = 32 * c + 8 * grp;
+      u32x4_t x = {0u, 0u, 0u, 0u};
+      if (ok && d0 < D) x = ldg16(qp + d0);
+      qf[t][c] = as_bf16x8(x);
+    }
+  }
+  // vmcnt(0) as a builtin, so that the compiler knows the Q fragments have
+  // landed; the prologue tiles are waited for along with them.
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+
+  constexpr int kAhead = (NST - 2) * G::LPT;  // copies allowed in flight after tile it
+  static_assert(kAhead < 64, "vmcnt holds at most 63");
+  for (int it = 0; it < ntiles; ++it) {
+    if (it + NST - 2 < ntiles)
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(kAhead));  // tile it landed (this thread's copies)
+    else
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));       // near the end: everything landed
+    __syncthreads();                                   // everyone's copies; stage (it-1) % NST is free
+    if (it + NST - 1 < ntiles) issue(it + NST - 1);
+    compute_tile(stage + (it % NST) * G::STAGE_B, kbeg + it * BN);
+  }
+
+  float l_tot[QT];
+#pragma unroll
+  for (int t = 0; t < QT; ++t) l_tot[t] = group_sum(l_run[t]);
+
+  if (!wave_active) return;
+  if constexpr (!SPLIT) {
+#pragma unroll
+    for (int t = 0; t < QT; ++t) {
+      const int r = rw0 + 16 * t + col;
+      if (r >= p.Mp) continue;
+      const int s = r / g, hh = r - s * g;
+      const float l = l_tot[t];
+      const float inv = (l > 0.f) ? 1.0f / l : 0.f;
       uint16_t* op = p.out + ((size_t)(b * p.Sq + s) * p.Hq + hk * g + hh) * D;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
+      for (int dt = 0; dt < G::DT; ++dt) {
         const int d = 16 * dt + 4 * grp;
         if (d < D) {
           u32x2_t w = {pack_bf16x2(oacc[dt][t][0] * inv, oacc[dt][t][1] * inv),
@@ -310,111 +479,158 @@ fwd_kernel(const FwdParams p) {
         const float lse = (l > 0.f) ? (m_run[t] + __log2f(l)) * kLn2 : -INFINITY;
         p.lse[((size_t)b * p.Hq + hk * g + hh) * p.Sq + s] = lse;
       }
-    } else {
-      // Partial for this key range: normalised O, the running max (log2
-      // units) and the row sum.  An empty range stores l = 0.
-      const size_t prow = ((size_t)blockIdx.z * gridDim.y + bh) * p.Mp + r;
+    }
+  } else {
+    // ---- Partial of this key range: O/l, m (log2 units), l; empty: l = 0.
+    // Merged by combine_kernel, launched right after on the same stream.
+    const size_t slot_base = ((size_t)bh * p.nrb + blk.rb) * p.zmax;
+#pragma unroll
+    for (int t = 0; t < QT; ++t) {
+      const int rl = wave * 16 * QT + 16 * t + col;  // row within the block
+      if (row0 + rl >= p.Mp) continue;
+      const size_t prow = (slot_base + blk.z) * G::ROWS_WG + rl;
+      const float l = l_tot[t];
+      const float inv = (l > 0.f) ? 1.0f / l : 0.f;
       float* po = p.ws_o + prow * D;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
+      for (int dt = 0; dt < G::DT; ++dt) {
         const int d = 16 * dt + 4 * grp;
-        if (d < D) {
-          f32x4_t w = oacc[dt][t] * inv;
-          *reinterpret_cast<f32x4_t*>(po + d) = w;
-        }
+        if (d < D) *reinterpret_cast<f32x4_t*>(po + d) = oacc[dt][t] * inv;
       }
-      if (grp == 0) {
-        p.ws_ml[2 * prow] = m_run[t];
-        p.ws_ml[2 * prow + 1] = l;
-      }
+      if (grp == 0)
+        *reinterpret_cast<u32x2_t*>(p.ws_ml + 2 * prow) = u32x2_t{__float_as_uint(m_run[t]), __float_as_uint(l)};
     }
   }
 }
 
-// Merge the split partials of one packed row, in split order:
-//   M = max_s m_s over non-empty splits, w_s = l_s * 2^(m_s - M),
-//   out = sum_s w_s * Ohat_s / sum_s w_s,  lse = ln2 * (M + log2 sum_s w_s).
-// One thread per (packed row, 8 head-dim elements).
-template <int D>
+// Merge of the split-KV partials of one packed row and 8 head-dim elements
+// per thread, in split order (deterministic):
+//   M = max_z m_z over non-empty splits, w_z = l_z 2^(m_z - M),
+//   out = sum_z w_z Ohat_z / sum_z w_z,   lse = ln2 (M + log2 sum_z w_z).
+// The running form below rescales as M grows, which is the same sum.
+template <int D, int ROWS_WG, bool CAUSAL>
 __global__ void __launch_bounds__(256)
-combine_kernel(const FwdParams p, int nsplit, int BH) {
+combine_kernel(const FwdParams p) {
   constexpr int CPR = D / 8;
   const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-  const long long total = (long long)BH * p.Mp * CPR;
-  if (i >= total) return;
-  const int ch = (int)(i % CPR);
-  const long long rr = i / CPR;
-  const int r = (int)(rr % p.Mp);
-  const int bh = (int)(rr / p.Mp);
-  const int b = bh / p.Hkv, hk = bh - b * p.Hkv;
+  const long long per_bh = (long long)p.nrb * ROWS_WG * CPR;
+  const int bh = (int)(i / per_bh);
+  if (bh >= p.B * p.Hkv) return;
+  const int rem = (int)(i - (long long)bh * per_bh);
+  const int rb = rem / (ROWS_WG * CPR);
+  const int rl = (rem / CPR) % ROWS_WG;
+  const int ch = rem % CPR;
+  const int r = rb * ROWS_WG + rl;
+  if (r >= p.Mp) return;
   const int g = p.g;
-  const size_t split_stride = (size_t)BH * p.Mp;
-
-  float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) {
-    const size_t prow = s * split_stride + rr;
-    const float l = p.ws_ml[2 * prow + 1];
-    if (l > 0.f) M = fmaxf(M, p.ws_ml[2 * prow]);
+  const int b = bh / p.Hkv, hk = bh - b * p.Hkv;
+  int nz = p.zmax;
+  if constexpr (CAUSAL) {
+    const int kmax = (min((rb + 1) * ROWS_WG, p.Mp) - 1) / g + 1;
+    nz = (kmax + p.kps - 1) / p.kps;
   }
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float L = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
-    const size_t prow = s * split_stride + rr;
-    const float l = p.ws_ml[2 * prow + 1];
-    if (!(l > 0.f)) continue;
-    const float w = l * __builtin_amdgcn_exp2f(p.ws_ml[2 * prow] - M);
-    L += w;
-    const f32x4_t* po = reinterpret_cast<const f32x4_t*>(p.ws_o + prow * D + 8 * ch);
-    const f32x4_t a0 = po[0], a1 = po[1];
+  const size_t slot_base = ((size_t)bh * p.nrb + rb) * p.zmax;
+  float M = -INFINITY, L = 0.f;
+  f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+  constexpr int U = 4;  // splits whose loads are in flight together
+  for (int z0 = 0; z0 < nz; z0 += U) {
+    u32x2_t ml[U];
+    f32x4_t o0[U], o1[U];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc[e] += w * a0[e];
-      acc[4 + e] += w * a1[e];
+    for (int u = 0; u < U; ++u) {
+      const int z = min(z0 + u, nz - 1);
+      const size_t prow = (slot_base + z) * ROWS_WG + rl;
+      ml[u] = *reinterpret_cast<const u32x2_t*>(p.ws_ml + 2 * prow);
+      const f32x4_t* po = reinterpret_cast<const f32x4_t*>(p.ws_o + prow * D + 8 * ch);
+      o0[u] = po[0];
+      o1[u] = po[1];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float lz = __uint_as_float(ml[u][1]);
+      if (z0 + u >= nz || !(lz > 0.f)) continue;
+      const float mz = __uint_as_float(ml[u][0]);
+      const float m_new = fmaxf(M, mz);
+      const float alpha = __builtin_amdgcn_exp2f(M - m_new);  // 0 while M = -inf
+      const float w = lz * __builtin_amdgcn_exp2f(mz - m_new);
+      L = L * alpha + w;
+      a0 = a0 * alpha + w * o0[u];
+      a1 = a1 * alpha + w * o1[u];
+      M = m_new;
     }
   }
-  const int sq = r / g, hh = r - sq * g;
+  const int s = r / g, hh = r - s * g;
   const float inv = (L > 0.f) ? 1.0f / L : 0.f;
-  u32x4_t o;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
-  *reinterpret_cast<u32x4_t*>(p.out + ((size_t)(b * p.Sq + sq) * p.Hq + hk * g + hh) * D + 8 * ch) = o;
+  const u32x4_t o = {pack_bf16x2(a0[0] * inv, a0[1] * inv), pack_bf16x2(a0[2] * inv, a0[3] * inv),
+                     pack_bf16x2(a1[0] * inv, a1[1] * inv), pack_bf16x2(a1[2] * inv, a1[3] * inv)};
+  *reinterpret_cast<u32x4_t*>(p.out + ((size_t)(b * p.Sq + s) * p.Hq + hk * g + hh) * D + 8 * ch) = o;
   if (ch == 0 && p.lse != nullptr) {
     const float lse = (L > 0.f) ? (M + __log2f(L)) * kLn2 : -INFINITY;
-    p.lse[((size_t)b * p.Hq + hk * g + hh) * p.Sq + sq] = lse;
+    p.lse[((size_t)b * p.Hq + hk * g + hh) * p.Sq + s] = lse;
   }
 }
 
-template <int D, int QT, int NW, int BN, bool CAUSAL, bool SPLIT>
-static hipError_t launch_one(const FwdParams& p, const LaunchPlan& plan, hipStream_t stream) {
-  constexpr int ROWS_WG = NW * 16 * QT;
-  dim3 grid((p.Mp + ROWS_WG - 1) / ROWS_WG, p.B * p.Hkv, SPLIT ? plan.nsplit : 1);
-  hipLaunchKernelGGL((fwd_kernel<D, QT, NW, BN, CAUSAL, SPLIT>), grid, dim3(NW * 64), 0, stream, p);
+// ------------------------------------------------------------------ launch
+
+template <int D, int QT, int NW, int BN, int NST, bool CAUSAL, bool SPLIT>
+static hipError_t launch_variant(const FwdParams& p, const LaunchPlan& plan, hipStream_t stream) {
+  using G = Geo<D, QT, NW, BN>;
+  const int nrb = (p.Mp + G::ROWS_WG - 1) / G::ROWS_WG;
+  dim3 grid;
+  if (CAUSAL) {
+    int items = 0;
+    for (int rb = 0; rb < nrb; ++rb) {
+      const int kmax = (std::min((rb + 1) * G::ROWS_WG, p.Mp) - 1) / p.g + 1;
+      items += SPLIT ? (kmax + p.kps - 1) / p.kps : 1;
+    }
+    grid = dim3(items, p.B * p.Hkv, 1);
+  } else {
+    grid = dim3(nrb, p.B * p.Hkv, SPLIT ? plan.nsplit : 1);
+  }
+  hipLaunchKernelGGL((fwd_kernel<D, QT, NW, BN, NST, CAUSAL, SPLIT>), grid, dim3(NW * 64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !SPLIT) return e;
-  const long long threads = (long long)p.B * p.Hkv * p.Mp * (D / 8);
-  dim3 cgrid((unsigned)((threads + 255) / 256));
-  hipLaunchKernelGGL((combine_kernel<D>), cgrid, dim3(256), 0, stream, p, plan.nsplit, p.B * p.Hkv);
+  const long long threads = (long long)p.B * p.Hkv * nrb * G::ROWS_WG * (D / 8);
+  hipLaunchKernelGGL((combine_kernel<D, G::ROWS_WG, CAUSAL>), dim3((unsigned)((threads + 255) / 256)), dim3(256),
+                     0, stream, p);
   return hipGetLastError();
 }
 
-template <int D>
-static hipError_t launch_d(const FwdParams& p, const LaunchPlan& plan, hipStream_t stream) {
-  constexpr int QT = 2, NW = 4, BN = 64;
-  if (plan.causal) return launch_one<D, QT, NW, BN, true, false>(p, plan, stream);
-  if (plan.nsplit > 0) return launch_one<D, QT, NW, BN, false, true>(p, plan, stream);
-  return launch_one<D, QT, NW, BN, false, false>(p, plan, stream);
+// The compiled variants.  Each entry: head dim, rows per wave / 16, waves,
+// keys per tile, K/V stages in LDS.  Every variant is built with and without
+// causal masking and with and without the split-KV partial output.
+#define FA_VARIANTS(X) \
+  X(64, 1, 4, 64, 2)   \
+  X(64, 2, 4, 64, 2)   \
+  X(72, 1, 4, 64, 2)   \
+  X(72, 1, 4, 64, 4)   \
+  X(72, 2, 4, 64, 2)   \
+  X(256, 1, 4, 32, 2)  \
+  X(256, 1, 4, 32, 4)  \
+  X(256, 2, 4, 32, 2)  \
+  X(256, 2, 4, 32, 4)  \
+  X(256, 2, 4, 64, 2)
+
+bool variant_exists(int D, int qt, int nw, int bn, int nst) {
+#define FA_MATCH(d_, q_, n_, b_, s_) \
+  if (D == d_ && qt == q_ && nw == n_ && bn == b_ && nst == s_) return true;
+  FA_VARIANTS(FA_MATCH)
+#undef FA_MATCH
+  return false;
 }
 
-int plan_rows_per_wg(int /*D*/) { return 4 * 16 * 2; }
-int plan_block_keys(int /*D*/) { return 64; }
-
 hipError_t launch_fwd(const FwdParams& p, const LaunchPlan& plan, hipStream_t stream) {
-  switch (plan.D) {
-    case 64: return launch_d<64>(p, plan, stream);
-    case 72: return launch_d<72>(p, plan, stream);
-    case 256: return launch_d<256>(p, plan, stream);
-    default: return hipErrorInvalidValue;
+#define FA_DISPATCH(d_, q_, n_, b_, s_)                                                          \
+  if (plan.D == d_ && plan.qt == q_ && plan.nw == n_ && plan.bn == b_ && plan.nst == s_) {        \
+    if (plan.causal)                                                                             \
+      return plan.split ? launch_variant<d_, q_, n_, b_, s_, true, true>(p, plan, stream)        \
+                        : launch_variant<d_, q_, n_, b_, s_, true, false>(p, plan, stream);      \
+    return plan.split ? launch_variant<d_, q_, n_, b_, s_, false, true>(p, plan, stream)         \
+                      : launch_variant<d_, q_, n_, b_, s_, false, false>(p, plan, stream);       \
   }
+  FA_VARIANTS(FA_DISPATCH)
+#undef FA_DISPATCH
+  return hipErrorInvalidValue;
 }
 
 }  // namespace fa

@@ -9,31 +9,37 @@ namespace fa {
 
 // Everything a forward launch needs, by value (kernel argument).
 struct FwdParams {
-  const uint16_t* q;   // [B, Sq, Hq, D] bf16
-  const uint16_t* k;   // [B, Sk, Hkv, D] bf16
-  const uint16_t* v;   // [B, Sk, Hkv, D] bf16
-  uint16_t* out;       // [B, Sq, Hq, D] bf16
-  float* lse;          // [B, Hq, Sq] fp32 or null
+  const uint16_t* q;       // [B, Sq, Hq, D] bf16
+  const uint16_t* k;       // [B, Sk, Hkv, D] bf16
+  const uint16_t* v;       // [B, Sk, Hkv, D] bf16
+  uint16_t* out;           // [B, Sq, Hq, D] bf16
+  float* lse;              // [B, Hq, Sq] fp32 or null
   const int32_t* seqused;  // [B] int32 on the device, or null
-  float* ws_o;         // split partials: [nsplit, B*Hkv, Mp, D] fp32
-  float* ws_ml;        // split partials: [nsplit, B*Hkv, Mp, 2] fp32 (m, l)
+  // Split-KV workspace (split variants only).  Partial rows are indexed
+  // ((bh * nrb + row_block) * zmax + split) * rows_per_block + row_in_block.
+  float* ws_o;             // partial O / l, fp32, D per partial row
+  float* ws_ml;            // partial (m in log2 units, l), fp32 pairs
   int B, Sq, Sk, Hq, Hkv;
-  int g;               // Hq / Hkv
-  int Mp;              // packed rows per (batch, kv head) = Sq * g
-  int kps;             // keys per split (multiple of the key tile), split path only
-  float scale_log2;    // scale * log2(e)
+  int g;                   // Hq / Hkv
+  int Mp;                  // packed rows per (batch, kv head) = Sq * g
+  int kps;                 // keys per split (multiple of the key tile), split variants only
+  int nrb;                 // row blocks per (batch, kv head)
+  int zmax;                // most splits of any row block
+  float scale_log2;        // scale * log2(e)
 };
 
 struct LaunchPlan {
   int D;
+  int qt;                  // rows per wave / 16
+  int nw;                  // waves per workgroup
+  int bn;                  // keys per tile
+  int nst;                 // K/V tile stages in LDS
   bool causal;
-  int nsplit;          // 0: single pass; >= 1: split-KV path with that many splits
+  bool split;
+  int nsplit;              // non-causal split count (grid.z)
 };
 
-// Tile geometry the host needs for planning.
-int plan_rows_per_wg(int D);
-int plan_block_keys(int D);
-
+bool variant_exists(int D, int qt, int nw, int bn, int nst);
 hipError_t launch_fwd(const FwdParams& p, const LaunchPlan& plan, hipStream_t stream);
 
 }  // namespace fa

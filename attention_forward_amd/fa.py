@@ -30,7 +30,8 @@ FA_ERR_WORKSPACE = 6
 FA_ERR_LAUNCH = 7
 FA_ERR_ALIAS = 8
 
-EXPORTS = ("fa_fwd", "fa_fwd_workspace_bytes", "fa_set_workspace", "fa_status_string", "fa_abi_version")
+EXPORTS = ("fa_fwd", "fa_fwd_workspace_bytes", "fa_set_workspace", "fa_fwd_variant",
+           "fa_fwd_variant_workspace_bytes", "fa_fwd_plan", "fa_status_string", "fa_abi_version")
 
 _lib = None
 _lib_lock = threading.Lock()
@@ -62,6 +63,13 @@ def load_library():
         lib.fa_fwd_workspace_bytes.argtypes = [i32] * 7
         lib.fa_set_workspace.restype = i32
         lib.fa_set_workspace.argtypes = [vp, ctypes.c_size_t]
+        lib.fa_fwd_variant.restype = i32
+        lib.fa_fwd_variant.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, f32,
+                                       i32, i32, i32, i32, i32, vp]
+        lib.fa_fwd_variant_workspace_bytes.restype = ctypes.c_size_t
+        lib.fa_fwd_variant_workspace_bytes.argtypes = [i32] * 12
+        lib.fa_fwd_plan.restype = i32
+        lib.fa_fwd_plan.argtypes = [i32] * 7 + [ctypes.POINTER(i32)] * 5
         lib.fa_status_string.restype = ctypes.c_char_p
         lib.fa_status_string.argtypes = [i32]
         lib.fa_abi_version.restype = i32
@@ -81,6 +89,28 @@ def fa_fwd(q, k, v, out, lse, B, Sq, Sk, Hq, Hkv, D, causal, seqused_k, scale, s
 
 def fa_fwd_workspace_bytes(B, Sq, Sk, Hq, Hkv, D, causal) -> int:
     return int(load_library().fa_fwd_workspace_bytes(B, Sq, Sk, Hq, Hkv, D, int(causal)))
+
+
+def fa_fwd_variant(q, k, v, out, lse, B, Sq, Sk, Hq, Hkv, D, causal, seqused_k, scale,
+                   qt, nw, bn, nst, kps, stream) -> int:
+    """C ``fa_fwd_variant``: fa_fwd with an explicit kernel variant."""
+    return load_library().fa_fwd_variant(q or None, k or None, v or None, out or None, lse or None,
+                                         B, Sq, Sk, Hq, Hkv, D, int(causal), seqused_k or None,
+                                         ctypes.c_float(scale), qt, nw, bn, nst, kps, stream or None)
+
+
+def fa_fwd_variant_workspace_bytes(B, Sq, Sk, Hq, Hkv, D, causal, qt, nw, bn, nst, kps) -> int:
+    return int(load_library().fa_fwd_variant_workspace_bytes(B, Sq, Sk, Hq, Hkv, D, int(causal),
+                                                             qt, nw, bn, nst, kps))
+
+
+def fa_fwd_plan(B, Sq, Sk, Hq, Hkv, D, causal):
+    """(qt, nw, bn, nst, kps) that fa_fwd uses for this shape."""
+    out = [ctypes.c_int() for _ in range(5)]
+    rc = load_library().fa_fwd_plan(B, Sq, Sk, Hq, Hkv, D, int(causal), *[ctypes.byref(x) for x in out])
+    if rc != FA_OK:
+        raise FAError(rc, "fa_fwd_plan")
+    return tuple(x.value for x in out)
 
 
 def fa_set_workspace(dev_ptr, nbytes) -> int:
@@ -119,13 +149,14 @@ def ensure_workspace(device, nbytes: int):
 
 
 def attention(q, k, v, *, causal=False, seqused_k=None, scale=None, out=None, lse=None,
-              return_lse=True):
+              return_lse=True, variant=None):
     """out, lse = softmax(scale * q k^T + mask) v for bf16 BSHD cuda tensors.
 
     q [B, Sq, Hq, D]; k, v [B, Sk, Hkv, D]; seqused_k int32 [B] on the same
     device or None.  ``scale`` defaults to 1/sqrt(D).  Returns (out, lse)
     with lse [B, Hq, Sq] float32 (None when ``return_lse`` is False and no
-    ``lse`` tensor is passed).
+    ``lse`` tensor is passed).  ``variant`` = (qt, nw, bn, nst, kps) runs
+    that kernel variant through fa_fwd_variant instead of fa_fwd's choice.
     """
     import torch
 
@@ -157,12 +188,21 @@ def attention(q, k, v, *, causal=False, seqused_k=None, scale=None, out=None, ls
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     causal = bool(causal)
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), 0 if lse is None else lse.data_ptr())
+    sq = 0 if seqused_k is None else seqused_k.data_ptr()
     with torch.cuda.device(dev):
-        ensure_workspace(dev, fa_fwd_workspace_bytes(B, Sq, Sk, Hq, Hkv, D, causal))
         stream = torch.cuda.current_stream(dev).cuda_stream
-        rc = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                    0 if lse is None else lse.data_ptr(), B, Sq, Sk, Hq, Hkv, D, causal,
-                    0 if seqused_k is None else seqused_k.data_ptr(), float(scale), stream)
+        if variant is None:
+            ensure_workspace(dev, fa_fwd_workspace_bytes(B, Sq, Sk, Hq, Hkv, D, causal))
+            rc = fa_fwd(*ptrs, B, Sq, Sk, Hq, Hkv, D, causal, sq, float(scale), stream)
+            where = "fa_fwd"
+        else:
+            qt, nw, bn, nst, kps = variant
+            ensure_workspace(dev, fa_fwd_variant_workspace_bytes(B, Sq, Sk, Hq, Hkv, D, causal,
+                                                                 qt, nw, bn, nst, kps))
+            rc = fa_fwd_variant(*ptrs, B, Sq, Sk, Hq, Hkv, D, causal, sq, float(scale), qt, nw, bn, nst, kps,
+                                stream)
+            where = "fa_fwd_variant"
     if rc != FA_OK:
-        raise FAError(rc, "fa_fwd")
+        raise FAError(rc, where)
     return out, lse

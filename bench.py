@@ -154,7 +154,7 @@ def dispatch_floor_us(device, steps=200):
     return ev / steps * 1e6
 
 
-def cpu_baseline(w, budget_s=10.0, max_runs=50):
+def cpu_baseline(w, budget_s=10.0, max_runs=100000):
     """The fp64 oracle as it stands, repeated on the full workload until
     `budget_s` seconds of host time are spent (at least one run)."""
     import numpy as np
@@ -181,6 +181,64 @@ def cpu_baseline(w, budget_s=10.0, max_runs=50):
             "ms_per_call": round(el / runs * 1e3, 2)}
 
 
+CALIB_BYTES = 256 << 20  # device-to-device copy used to calibrate the byte counters
+
+
+def traffic_probe(w, reps, device):
+    """Eager calls of the workload plus a device-to-device copy of
+    CALIB_BYTES, for a rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE pass."""
+    import torch
+
+    r = Runner(w, device)
+    src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=device).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+        r.step(torch.cuda.current_stream(device).cuda_stream)
+    torch.cuda.synchronize()
+
+
+def ingest_traffic(workload, fetch_csv, write_csv, out_path=TRAFFIC_FILE):
+    """HBM bytes per launch of the attention kernels from the counter CSVs
+    of two rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE; KiB per
+    dispatch).  Each counter is scaled by what it reads for the calibration
+    copy of CALIB_BYTES (which moves exactly CALIB_BYTES each way)."""
+    import csv
+    import statistics
+
+    def per_kernel(path, counter):
+        vals = {}
+        for row in csv.DictReader(open(path)):
+            if row["Counter_Name"] != counter:
+                continue
+            vals.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+        return vals
+
+    out = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        vals = per_kernel(path, counter)
+        calib = max((statistics.median(v) for k, v in vals.items() if "copyBuffer" in k or "copy" in k.lower()),
+                    default=None)
+        if not calib:
+            raise RuntimeError(f"no calibration copy found in {path}")
+        factor = CALIB_BYTES / (calib * 1024.0)
+        kb = sum(statistics.median(v) for k, v in vals.items() if "fa::" in k)
+        out[counter] = {"kib_per_launch": kb, "calibration_kib": calib, "factor": factor,
+                        "bytes_per_launch": kb * 1024.0 * factor}
+    entry = {"kernel_sha": kernel_sha(), "fetch": out["FETCH_SIZE"], "write": out["WRITE_SIZE"],
+             "bytes_per_launch": out["FETCH_SIZE"]["bytes_per_launch"] + out["WRITE_SIZE"]["bytes_per_launch"]}
+    try:
+        with open(out_path) as f:
+            table = json.load(f)
+    except (OSError, ValueError):
+        table = {}
+    table[workload] = entry
+    with open(out_path, "w") as f:
+        json.dump(table, f, indent=1, sort_keys=True)
+    return entry
+
+
 def measure(w, steps, warmup, device):
     r = Runner(w, device)
     wall, ev = time_graph(r.step, steps, warmup, device)
@@ -197,7 +255,14 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-all", action="store_true", help="skip the per-workload table")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--traffic-probe", type=int, default=0, metavar="REPS",
+                    help="only run REPS eager calls plus a calibration copy (for rocprofv3 --pmc)")
+    ap.add_argument("--ingest-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter CSVs into profiles/traffic.json and exit")
     a = ap.parse_args(argv)
+    if a.ingest_traffic:
+        print(json.dumps(ingest_traffic(a.workload, *a.ingest_traffic)))
+        return 0
     if a.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {a.gpus} is not supported (this library has no "
               "multi-GPU path; run with --gpus 1)", file=sys.stderr)
@@ -211,6 +276,10 @@ def main(argv=None):
         return 1
     device = torch.device("cuda:0")
     w = WORKLOADS[a.workload]
+    if a.traffic_probe:
+        traffic_probe(w, a.traffic_probe, device)
+        print(f"traffic probe done: {w.name} x{a.traffic_probe}", flush=True)
+        return 0
     r, wall, ev, flops, nbytes = measure(w, a.steps, a.warmup, device)
     sec_launch = ev / a.steps
     bound = binding_roofline(flops, nbytes)

@@ -43,8 +43,9 @@ extern "C" {
 enum {
   FA_OK = 0,
   FA_ERR_NULL = 1,        /* a required pointer is NULL */
-  FA_ERR_SHAPE = 2,       /* a size is < 1, Hq % Hkv != 0, or a size overflows 32-bit indexing */
-  FA_ERR_UNSUPPORTED = 3, /* D not in {64, 72, 256}; causal with Sq != Sk or with seqused_k */
+  FA_ERR_SHAPE = 2,       /* a size is < 1, Hq % Hkv != 0, or a size overflows 32-bit indexing
+                             (element counts of q and k, or Sk*Hkv*D*2 bytes per batch entry, >= 2^31) */
+  FA_ERR_UNSUPPORTED = 3, /* D not in {64, 72, 256}; causal with Sq != Sk or with seqused_k; variant not compiled */
   FA_ERR_ALIGN = 4,       /* q, k, v, out not 16-byte aligned; lse or seqused_k not 4-byte aligned */
   FA_ERR_SCALE = 5,       /* scale not finite or not > 0 */
   FA_ERR_WORKSPACE = 6,   /* the split-KV path needs a workspace that is missing or too small */
@@ -71,9 +72,10 @@ enum {
  *   D is 64, 72 or 256.
  *   stream     HIP stream for the launch (NULL = default stream).
  *
- * Some shapes (few packed query rows, long key buffers) take a split-KV
- * path that needs a workspace registered with fa_set_workspace() on the
- * current device; fa_fwd_workspace_bytes() says how many bytes (0 when the
+ * Shapes with few packed query rows per compute unit take a split-KV path
+ * (several workgroups per row block write partial results that a second
+ * kernel on the same stream merges in fixed order) that needs a workspace
+ * registered with fa_set_workspace() on the current device; fa_fwd_workspace_bytes() says how many bytes (0 when the
  * single-pass path is used).  Calls that share one workspace must not run
  * concurrently (one stream at a time per device).
  *
@@ -89,10 +91,37 @@ size_t fa_fwd_workspace_bytes(int B, int Sq, int Sk, int Hq, int Hkv, int D, int
 
 /* Registers a caller-owned device buffer as the split-KV workspace of the
  * current HIP device (replacing any earlier one; NULL/0 unregisters).  The
- * buffer needs no initialisation and must outlive every fa_fwd call queued
- * with it.  Not thread-safe against concurrent fa_fwd calls.
- * Returns FA_OK, or FA_ERR_NULL for a NULL pointer with bytes > 0. */
+ * buffer must be 256-byte aligned; it needs no initialisation.  It must
+ * outlive every fa_fwd call queued with it, and calls sharing it must not
+ * overlap in time (e.g. run them on one stream).  Not thread-safe against
+ * concurrent fa_fwd calls.
+ * Returns FA_OK, FA_ERR_NULL for a NULL pointer with bytes > 0, or
+ * FA_ERR_LAUNCH when no HIP device is current. */
 int fa_set_workspace(void* dev_ptr, size_t bytes);
+
+/* Tuning and testing entry points.  fa_fwd picks its kernel variant from
+ * the shape alone; these name one explicitly so that every compiled variant
+ * can be timed and checked:
+ *   qt   rows per wavefront / 16  (1 or 2)
+ *   nw   wavefronts per workgroup (4)
+ *   bn   keys per tile            (32 or 64)
+ *   nst  K/V tile stages in LDS   (2 or 4)
+ *   kps  keys per split-KV range  (0: single pass; else a multiple of bn)
+ * A combination that is not compiled returns FA_ERR_UNSUPPORTED.  Other
+ * arguments, checks and errors are those of fa_fwd. */
+int fa_fwd_variant(const void* q, const void* k, const void* v, void* out, float* lse,
+                   int B, int Sq, int Sk, int Hq, int Hkv, int D, int causal,
+                   const int32_t* seqused_k, float scale, int qt, int nw, int bn, int nst, int kps,
+                   hipStream_t stream);
+
+/* Workspace bytes for fa_fwd_variant with that variant (0: none or invalid). */
+size_t fa_fwd_variant_workspace_bytes(int B, int Sq, int Sk, int Hq, int Hkv, int D, int causal,
+                                      int qt, int nw, int bn, int nst, int kps);
+
+/* The variant fa_fwd chooses for a shape, written to *qt, *nw, *bn, *nst,
+ * *kps.  Returns FA_OK or the shape error fa_fwd would return. */
+int fa_fwd_plan(int B, int Sq, int Sk, int Hq, int Hkv, int D, int causal,
+                int* qt, int* nw, int* bn, int* nst, int* kps);
 
 /* Static, NUL-terminated description of a status code. */
 const char* fa_status_string(int code);

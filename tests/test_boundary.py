@@ -101,11 +101,33 @@ def test_workspace_sizes(lib):
     assert n > 0
     # ... and the size depends on the shape only, never on seqused_k values
     assert n == fa.fa_fwd_workspace_bytes(1, 41, 1056, 8, 1, 256, 0)
-    # large problems and causal problems run single-pass
-    assert fa.fa_fwd_workspace_bytes(1, 1024, 1024, 8, 1, 256, 0) == 0
-    assert fa.fa_fwd_workspace_bytes(1, 2048, 2048, 8, 1, 256, 1) == 0
+    # a single-pass plan needs none; a split plan needs some
+    for shape in [(1, 1024, 1024, 8, 1, 256, 0), (1, 2048, 2048, 8, 1, 256, 1), (1, 64, 64, 1, 1, 64, 0),
+                  (3, 256, 256, 16, 16, 72, 0)]:
+        assert (fa.fa_fwd_workspace_bytes(*shape) > 0) == (fa.fa_fwd_plan(*shape)[4] > 0)
     assert fa.fa_fwd_workspace_bytes(1, 64, 64, 1, 1, 64, 0) == 0
     assert fa.fa_fwd_workspace_bytes(0, 64, 64, 1, 1, 64, 0) == 0
+
+
+def test_plan_and_variant_sizes(lib):
+    assert fa.fa_fwd_plan(1, 41, 1056, 8, 1, 256, 0)[4] > 0      # small M: split keys
+    assert fa.fa_fwd_plan(3, 256, 256, 16, 16, 72, 0)[4] == 0    # enough rows: single pass
+    qt, nw, bn, nst, kps = fa.fa_fwd_plan(1, 41, 1056, 8, 1, 256, 0)
+    assert fa.fa_fwd_variant_workspace_bytes(1, 41, 1056, 8, 1, 256, 0, qt, nw, bn, nst, kps) == \
+        fa.fa_fwd_workspace_bytes(1, 41, 1056, 8, 1, 256, 0)
+    assert fa.fa_fwd_variant_workspace_bytes(1, 41, 1056, 8, 1, 256, 0, 3, 4, 64, 2, 0) == 0
+    assert fa.fa_fwd_variant_workspace_bytes(1, 41, 1056, 8, 1, 256, 0, 1, 4, 32, 2, 0) == 0
+
+
+def test_variant_rejections(lib):
+    args = [Q, K, V, O, L, 1, 64, 64, 8, 1, 256, 0, 0, 0.0625]
+    assert fa.fa_fwd_variant(*args, 3, 4, 64, 2, 0, 0) == fa.FA_ERR_UNSUPPORTED   # not compiled
+    assert fa.fa_fwd_variant(*args, 1, 4, 32, 3, 0, 0) == fa.FA_ERR_UNSUPPORTED   # no 3-stage build
+    assert fa.fa_fwd_variant(*args, 1, 4, 32, 2, 48, 0) == fa.FA_ERR_UNSUPPORTED  # kps % bn
+    assert fa.fa_fwd_variant(*args, 1, 4, 32, 2, -32, 0) == fa.FA_ERR_UNSUPPORTED
+    bad = list(args)
+    bad[0] = 0
+    assert fa.fa_fwd_variant(*bad, 1, 4, 32, 2, 0, 0) == fa.FA_ERR_NULL
 
 
 def test_set_workspace_null_with_size(lib):
