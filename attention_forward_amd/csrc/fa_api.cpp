@@ -45,7 +45,9 @@ struct Plan {
   size_t ws_o_bytes = 0, ws_ml_bytes = 0, ws_bytes = 0;
 };
 
-int rows_per_block(const fa::LaunchPlan& l) { return l.nw * 16 * l.qt; }
+// Packed rows one workgroup covers: its waves own different rows (kw == 1)
+// or all share the same 16*qt rows and split the keys (kw > 1).
+int rows_per_block(const fa::LaunchPlan& l) { return (l.kw > 1 ? 1 : l.nw) * 16 * l.qt; }
 
 // Fills in the derived fields (row blocks, split count, workspace layout) of
 // a plan whose variant and keys-per-split are set.  kps == 0: no split.
@@ -75,8 +77,9 @@ void finish_plan(Plan& pl, int B, int Sq, int Sk, int Hq, int Hkv, int causal) {
 }
 
 // Default variant for a shape: a function of the shape only (never of the
-// seqused_k values), so equal shapes always run the same kernel.  One wave
-// per 16 packed rows.  When the single-pass grid is at most half the compute
+// seqused_k values), so equal shapes always run the same kernel.  Head dim
+// 256 with at least 32 rows per compute unit runs the key-split kernel;
+// otherwise one wave per 16 packed rows.  When the single-pass grid is at most half the compute
 // units, the key range is split into fixed-size ranges, merged afterwards by
 // the combine kernel.  The range size depends on the grid size only, not on
 // the key buffer length, so a padded buffer and the same keys without the
@@ -89,8 +92,20 @@ Plan default_plan(int B, int Sq, int Sk, int Hq, int Hkv, int D, int causal) {
   const long long Mp = (long long)Sq * (Hq / Hkv);
   pl.launch.qt = 1;
   pl.launch.nw = 4;
+  pl.launch.kw = 1;
   pl.launch.bn = D == 256 ? 32 : 64;
   pl.launch.nst = 2;
+  if (D == 256 && cdiv(Mp, 32) * BH >= kTargetWorkgroups) {
+    // Enough rows for one key-split workgroup (32 rows, four waves over the
+    // keys) per compute unit: twice the rows per wave of the row-split
+    // kernel, so half the LDS reads per MFMA.
+    pl.launch.qt = 2;
+    pl.launch.kw = 4;
+    pl.launch.nst = 1;
+    pl.kps = 0;
+    finish_plan(pl, B, Sq, Sk, Hq, Hkv, causal);
+    return pl;
+  }
   const int rows = rows_per_block(pl.launch);
   const long long base = cdiv(Mp, rows) * BH;
   pl.kps = 0;
@@ -145,13 +160,14 @@ int check_args(const void* q, const void* k, const void* v, void* out, float* ls
 }
 
 // Variant given by the caller: checked against the compiled set.
-int variant_plan(Plan& pl, int B, int Sq, int Sk, int Hq, int Hkv, int D, int causal, int qt, int nw, int bn,
-                 int nst, int kps) {
-  if (!fa::variant_exists(D, qt, nw, bn, nst)) return FA_ERR_UNSUPPORTED;
+int variant_plan(Plan& pl, int B, int Sq, int Sk, int Hq, int Hkv, int D, int causal, int qt, int nw, int kw,
+                 int bn, int nst, int kps) {
+  if (!fa::variant_exists(D, qt, nw, kw, bn, nst)) return FA_ERR_UNSUPPORTED;
   if (kps < 0 || (kps > 0 && kps % bn != 0)) return FA_ERR_UNSUPPORTED;
   pl.launch.D = D;
   pl.launch.qt = qt;
   pl.launch.nw = nw;
+  pl.launch.kw = kw;
   pl.launch.bn = bn;
   pl.launch.nst = nst;
   pl.kps = kps;
@@ -226,10 +242,10 @@ size_t fa_fwd_workspace_bytes(int B, int Sq, int Sk, int Hq, int Hkv, int D, int
 }
 
 size_t fa_fwd_variant_workspace_bytes(int B, int Sq, int Sk, int Hq, int Hkv, int D, int causal, int qt, int nw,
-                                      int bn, int nst, int kps) {
+                                      int kw, int bn, int nst, int kps) {
   if (check_shape(B, Sq, Sk, Hq, Hkv, D, causal) != FA_OK) return 0;
   Plan pl;
-  if (variant_plan(pl, B, Sq, Sk, Hq, Hkv, D, causal, qt, nw, bn, nst, kps) != FA_OK) return 0;
+  if (variant_plan(pl, B, Sq, Sk, Hq, Hkv, D, causal, qt, nw, kw, bn, nst, kps) != FA_OK) return 0;
   return padded_ws_bytes(pl);
 }
 
@@ -253,23 +269,25 @@ int fa_fwd(const void* q, const void* k, const void* v, void* out, float* lse, i
 
 int fa_fwd_variant(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Sq, int Sk,
                    int Hq, int Hkv, int D, int causal, const int32_t* seqused_k, float scale, int qt, int nw,
-                   int bn, int nst, int kps, hipStream_t stream) {
+                   int kw, int bn, int nst, int kps, hipStream_t stream) {
   int rc = check_args(q, k, v, out, lse, B, Sq, Sk, Hq, Hkv, D, causal, seqused_k, scale);
   if (rc != FA_OK) return rc;
   Plan pl;
-  rc = variant_plan(pl, B, Sq, Sk, Hq, Hkv, D, causal, qt, nw, bn, nst, kps);
+  rc = variant_plan(pl, B, Sq, Sk, Hq, Hkv, D, causal, qt, nw, kw, bn, nst, kps);
   if (rc != FA_OK) return rc;
   return run(pl, q, k, v, out, lse, B, Sq, Sk, Hq, Hkv, causal, seqused_k, scale, stream);
 }
 
-int fa_fwd_plan(int B, int Sq, int Sk, int Hq, int Hkv, int D, int causal, int* qt, int* nw, int* bn, int* nst,
-                int* kps) {
+int fa_fwd_plan(int B, int Sq, int Sk, int Hq, int Hkv, int D, int causal, int* qt, int* nw, int* kw, int* bn,
+                int* nst, int* kps) {
   int rc = check_shape(B, Sq, Sk, Hq, Hkv, D, causal);
   if (rc != FA_OK) return rc;
-  if (qt == nullptr || nw == nullptr || bn == nullptr || nst == nullptr || kps == nullptr) return FA_ERR_NULL;
+  if (qt == nullptr || nw == nullptr || kw == nullptr || bn == nullptr || nst == nullptr || kps == nullptr)
+    return FA_ERR_NULL;
   const Plan pl = default_plan(B, Sq, Sk, Hq, Hkv, D, causal);
   *qt = pl.launch.qt;
   *nw = pl.launch.nw;
+  *kw = pl.launch.kw;
   *bn = pl.launch.bn;
   *nst = pl.launch.nst;
   *kps = pl.kps;

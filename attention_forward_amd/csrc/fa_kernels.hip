@@ -69,6 +69,9 @@ constexpr uint32_t kOutOfRange = 0x80000000u;     // a buffer offset past any ra
 // s_waitcnt immediate with vmcnt = n and expcnt / lgkmcnt left at their
 // maxima (vmcnt is split over bits 3:0 and 15:14).
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+// s_waitcnt immediate with lgkmcnt = 0 (every LDS access of this wave has
+// completed) and vmcnt / expcnt left at their maxima.
+constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
 
 __device__ __forceinline__ u32x4_t ldg16(const uint16_t* p) { return *reinterpret_cast<const u32x4_t*>(p); }
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t x) { return __builtin_bit_cast(bf16x8_t, x); }
@@ -152,6 +155,156 @@ struct Geo {
   static_assert(BN % 32 == 0, "key tile must be a multiple of 32");
   static_assert(DT * 16 * 2 <= VSTR, "V fragment reads stay inside a padded row");
 };
+
+// ---------------------------------------------------------------- tile phases
+// The three phases of one K/V tile for a wave that owns 16*QT packed rows.
+// G is the kernel geometry (head dim, key tile, LDS strides).  `kb` and
+// `vb` are this lane's read bases in the K and V tiles (see lane_bases).
+
+// Per-lane LDS read bases inside a stage: K fragment (row col of a 16-key
+// tile, chunk grp of a 32-element step), V transpose read (row 4grp + r,
+// head-dim 4q).
+template <class G>
+__device__ __forceinline__ void lane_bases(int lane, uint32_t& k_lane, uint32_t& v_lane) {
+  const int col = lane & 15, grp = lane >> 4, vr = lane >> 2 & 3, vq = lane & 3;
+  k_lane = col * G::KSTR + grp * 16;
+  v_lane = G::K_B + (4 * grp + vr) * G::VSTR + vq * 8;
+}
+
+// S^T = K * Q^T for one tile: lane (col, grp) gets query col, keys
+// 16mt + 4grp + r.  Fragment loads run a few steps ahead of the MFMAs that
+// use them; the scheduling barriers keep that order so LDS latency overlaps
+// MFMA work.
+template <class G, int QT>
+__device__ __forceinline__ void qk_tile(f32x4_t (&sacc)[G::MT][QT], const bf16x8_t (&qf)[QT][G::KC],
+                                        const uint8_t* kb, int grp) {
+  auto load_k = [&](int c, int mt) __attribute__((always_inline)) -> bf16x8_t {
+    if constexpr (4 * (G::KC - 1) + 3 >= G::CPR) {  // head dim not a multiple of 32 (D = 72)
+      if (4 * c + grp >= G::CPR) return as_bf16x8(u32x4_t{0u, 0u, 0u, 0u});
+    }
+    return as_bf16x8(*reinterpret_cast<const u32x4_t*>(kb + mt * 16 * G::KSTR + c * 64));
+  };
+  constexpr int PFK = G::KC < 3 ? G::KC : 3;
+#pragma unroll
+  for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+    for (int t = 0; t < QT; ++t) sacc[mt][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  bf16x8_t kf[G::KC][G::MT];
+#pragma unroll
+  for (int c = 0; c < PFK; ++c)
+#pragma unroll
+    for (int mt = 0; mt < G::MT; ++mt) kf[c][mt] = load_k(c, mt);
+#pragma unroll
+  for (int c = 0; c < G::KC; ++c) {
+    if (c + PFK < G::KC) {
+#pragma unroll
+      for (int mt = 0; mt < G::MT; ++mt) kf[c + PFK][mt] = load_k(c + PFK, mt);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+      for (int t = 0; t < QT; ++t)
+        sacc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[c][mt], qf[t][c], sacc[mt][t], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// V^T fragment for 32-key step kc and head-dim tile dt.  Lane 16grp+4r+q of
+// read h points at V row 32kc + 16h + 4grp + r, head-dim 16dt + 4q..+3; the
+// transpose read hands lane (col, grp) the four keys of that group at
+// head-dim 16dt + col, i.e. the slots P^T holds in elements 4h .. 4h+3.
+// Past the head dim (D = 72, dt = 4) the reads land in the row padding.
+template <class G>
+__device__ __forceinline__ bf16x8_t load_v(const uint8_t* vb, int kc, int dt) {
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vb + (32 * kc) * G::VSTR + dt * 32));
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vb + (32 * kc + 16) * G::VSTR + dt * 32));
+  const u32x4_t vw = {__builtin_bit_cast(u32x2_t, lo)[0], __builtin_bit_cast(u32x2_t, lo)[1],
+                      __builtin_bit_cast(u32x2_t, hi)[0], __builtin_bit_cast(u32x2_t, hi)[1]};
+  return as_bf16x8(vw);
+}
+
+// Online softmax of one tile on the raw scores (scale > 0, so the max
+// commutes with it): p = exp2(s * scale*log2e - m) in one fma + exp.  Keys
+// at or past kend, and for causal keys past the row's position, get p = 0.
+// Updates m_run / l_run, rescales O lazily, and packs P^T to bf16.
+template <class G, int QT, bool CAUSAL>
+__device__ __forceinline__ void softmax_tile(f32x4_t (&sacc)[G::MT][QT], uint32_t (&pk)[G::KVC][QT][4],
+                                             float (&m_run)[QT], float (&l_run)[QT],
+                                             f32x4_t (&oacc)[G::DT][QT], const int (&srow)[QT], int kt, int kend,
+                                             int s_lo, float c2, int grp) {
+  constexpr int BN = G::MT * 16;
+  const bool need_mask = (kt + BN > kend) || (CAUSAL && kt + BN - 1 > s_lo);
+#pragma unroll
+  for (int t = 0; t < QT; ++t) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float x = sacc[mt][t][r];
+        if (need_mask) {
+          const int key = kt + 16 * mt + 4 * grp + r;
+          bool ok = key < kend;
+          if constexpr (CAUSAL) ok = ok && key <= srow[t];
+          x = ok ? x : -INFINITY;
+          sacc[mt][t][r] = x;
+        }
+        mx = fmaxf(mx, x);
+      }
+    mx = group_max(mx) * c2;
+    const float m_new = fmaxf(m_run[t], mx);
+    if (__ballot(m_new > m_run[t] + kRescaleThreshold) != 0) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run[t] - m_new);  // 0 when m_run = -inf
+      m_run[t] = m_new;
+      l_run[t] *= alpha;
+#pragma unroll
+      for (int i = 0; i < G::DT; ++i) oacc[i][t] *= alpha;
+    }
+    const float m_neg = (m_run[t] == -INFINITY) ? 0.f : -m_run[t];
+    float lsum = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][t][r], c2, m_neg));
+        sacc[mt][t][r] = pv;
+        lsum += pv;
+      }
+    l_run[t] += lsum;
+#pragma unroll
+    for (int kc = 0; kc < G::KVC; ++kc) {
+      pk[kc][t][0] = pack_bf16x2(sacc[2 * kc][t][0], sacc[2 * kc][t][1]);
+      pk[kc][t][1] = pack_bf16x2(sacc[2 * kc][t][2], sacc[2 * kc][t][3]);
+      pk[kc][t][2] = pack_bf16x2(sacc[2 * kc + 1][t][0], sacc[2 * kc + 1][t][1]);
+      pk[kc][t][3] = pack_bf16x2(sacc[2 * kc + 1][t][2], sacc[2 * kc + 1][t][3]);
+    }
+  }
+}
+
+// O^T += V^T * P^T for one tile: lane (col, grp) gets query col, head-dim
+// 16dt + 4grp + r.
+template <class G, int QT>
+__device__ __forceinline__ void pv_tile(f32x4_t (&oacc)[G::DT][QT], const uint32_t (&pk)[G::KVC][QT][4],
+                                        const uint8_t* vb) {
+  constexpr int NV = G::KVC * G::DT;
+  constexpr int PFV = NV < 4 ? NV : 4;
+  bf16x8_t vf[NV];
+#pragma unroll
+  for (int i = 0; i < PFV; ++i) vf[i] = load_v<G>(vb, i / G::DT, i % G::DT);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int kc = i / G::DT, dt = i % G::DT;
+    if (i + PFV < NV) vf[i + PFV] = load_v<G>(vb, (i + PFV) / G::DT, (i + PFV) % G::DT);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < QT; ++t) {
+      const u32x4_t pw = {pk[kc][t][0], pk[kc][t][1], pk[kc][t][2], pk[kc][t][3]};
+      oacc[dt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[i], as_bf16x8(pw), oacc[dt][t], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
 
 struct RowBlock {
   int rb;      // row block index
@@ -270,11 +423,8 @@ fwd_kernel(const FwdParams p) {
     }
   };
 
-  // Per-lane LDS read bases: K fragment (row col of a 16-key tile, chunk
-  // grp of a 32-element step), V transpose read (row 4grp + r, head-dim 4q).
-  const int vr = lane >> 2 & 3, vq = lane & 3;
-  const uint32_t k_lane = col * G::KSTR + grp * 16;
-  const uint32_t v_lane = G::K_B + (4 * grp + vr) * G::VSTR + vq * 8;
+  uint32_t k_lane, v_lane;
+  lane_bases<G>(lane, k_lane, v_lane);
 
   // One K/V tile of the main loop, read from stage `st`.
   auto compute_tile = [&](const uint8_t* st, int kt) __attribute__((always_inline)) {
@@ -282,130 +432,12 @@ fwd_kernel(const FwdParams p) {
     if constexpr (CAUSAL) {
       if (kt > s_hi) return;  // tile entirely above this wave's diagonal
     }
-    const uint8_t* kb = st + k_lane;
-    const uint8_t* vb = st + v_lane;
-
-    // Fragment loads run a few steps ahead of the MFMAs that use them; the
-    // scheduling barriers keep that order so LDS latency overlaps MFMA work.
-    auto load_k = [&](int c, int mt) __attribute__((always_inline)) -> bf16x8_t {
-      if constexpr (4 * (G::KC - 1) + 3 >= G::CPR) {  // head dim not a multiple of 32 (D = 72)
-        if (4 * c + grp >= G::CPR) return as_bf16x8(u32x4_t{0u, 0u, 0u, 0u});
-      }
-      return as_bf16x8(*reinterpret_cast<const u32x4_t*>(kb + mt * 16 * G::KSTR + c * 64));
-    };
-    // V^T fragment for 32-key step kc and head-dim tile dt.  Lane 16grp+4r+q
-    // of read h points at V row 32kc + 16h + 4grp + r, head-dim 16dt + 4q..+3;
-    // the transpose read hands lane (col, grp) the four keys of that group at
-    // head-dim 16dt + col, i.e. the slots P^T holds in elements 4h .. 4h+3.
-    // Past the head dim (D = 72, dt = 4) the reads land in the row padding.
-    auto load_v = [&](int kc, int dt) __attribute__((always_inline)) -> bf16x8_t {
-      const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vb + (32 * kc) * G::VSTR + dt * 32));
-      const i16x4_t hi =
-          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vb + (32 * kc + 16) * G::VSTR + dt * 32));
-      const u32x4_t vw = {__builtin_bit_cast(u32x2_t, lo)[0], __builtin_bit_cast(u32x2_t, lo)[1],
-                          __builtin_bit_cast(u32x2_t, hi)[0], __builtin_bit_cast(u32x2_t, hi)[1]};
-      return as_bf16x8(vw);
-    };
-
-    // S^T = K * Q^T : lane (col, grp) gets query col, keys 16mt + 4grp + r.
-    constexpr int PFK = G::KC < 3 ? G::KC : 3;
     f32x4_t sacc[G::MT][QT];
-#pragma unroll
-    for (int mt = 0; mt < G::MT; ++mt)
-#pragma unroll
-      for (int t = 0; t < QT; ++t) sacc[mt][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    bf16x8_t kf[G::KC][G::MT];
-#pragma unroll
-    for (int c = 0; c < PFK; ++c)
-#pragma unroll
-      for (int mt = 0; mt < G::MT; ++mt) kf[c][mt] = load_k(c, mt);
-#pragma unroll
-    for (int c = 0; c < G::KC; ++c) {
-      if (c + PFK < G::KC) {
-#pragma unroll
-        for (int mt = 0; mt < G::MT; ++mt) kf[c + PFK][mt] = load_k(c + PFK, mt);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int mt = 0; mt < G::MT; ++mt)
-#pragma unroll
-        for (int t = 0; t < QT; ++t)
-          sacc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[c][mt], qf[t][c], sacc[mt][t], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-
-    // The first V^T fragments go out before the softmax arithmetic.
-    constexpr int NV = G::KVC * G::DT;
-    constexpr int PFV = NV < 4 ? NV : 4;
-    bf16x8_t vf[NV];
-#pragma unroll
-    for (int i = 0; i < PFV; ++i) vf[i] = load_v(i / G::DT, i % G::DT);
-    __builtin_amdgcn_sched_barrier(0);
-
-    // Softmax on the raw scores s (scale > 0, so max commutes with it):
-    // p = exp2(s * scale*log2e - m) in one fma + exp.
-    const bool need_mask = (kt + BN > kend) || (CAUSAL && kt + BN - 1 > s_lo);
     uint32_t pk[G::KVC][QT][4];
-#pragma unroll
-    for (int t = 0; t < QT; ++t) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int mt = 0; mt < G::MT; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float x = sacc[mt][t][r];
-          if (need_mask) {
-            const int key = kt + 16 * mt + 4 * grp + r;
-            bool ok = key < kend;
-            if constexpr (CAUSAL) ok = ok && key <= srow[t];
-            x = ok ? x : -INFINITY;
-            sacc[mt][t][r] = x;
-          }
-          mx = fmaxf(mx, x);
-        }
-      mx = group_max(mx) * c2;
-      const float m_new = fmaxf(m_run[t], mx);
-      if (__ballot(m_new > m_run[t] + kRescaleThreshold) != 0) {
-        const float alpha = __builtin_amdgcn_exp2f(m_run[t] - m_new);  // 0 when m_run = -inf
-        m_run[t] = m_new;
-        l_run[t] *= alpha;
-#pragma unroll
-        for (int i = 0; i < G::DT; ++i) oacc[i][t] *= alpha;
-      }
-      const float m_neg = (m_run[t] == -INFINITY) ? 0.f : -m_run[t];
-      float lsum = 0.f;
-#pragma unroll
-      for (int mt = 0; mt < G::MT; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][t][r], c2, m_neg));
-          sacc[mt][t][r] = pv;
-          lsum += pv;
-        }
-      l_run[t] += lsum;
-#pragma unroll
-      for (int kc = 0; kc < G::KVC; ++kc) {
-        pk[kc][t][0] = pack_bf16x2(sacc[2 * kc][t][0], sacc[2 * kc][t][1]);
-        pk[kc][t][1] = pack_bf16x2(sacc[2 * kc][t][2], sacc[2 * kc][t][3]);
-        pk[kc][t][2] = pack_bf16x2(sacc[2 * kc + 1][t][0], sacc[2 * kc + 1][t][1]);
-        pk[kc][t][3] = pack_bf16x2(sacc[2 * kc + 1][t][2], sacc[2 * kc + 1][t][3]);
-      }
-    }
+    qk_tile<G, QT>(sacc, qf, st + k_lane, grp);
+    softmax_tile<G, QT, CAUSAL>(sacc, pk, m_run, l_run, oacc, srow, kt, kend, s_lo, c2, grp);
     __builtin_amdgcn_sched_barrier(0);
-
-    // O^T += V^T * P^T : lane (col, grp) gets query col, head-dim 16dt + 4grp + r.
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int kc = i / G::DT, dt = i % G::DT;
-      if (i + PFV < NV) vf[i + PFV] = load_v((i + PFV) / G::DT, (i + PFV) % G::DT);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int t = 0; t < QT; ++t) {
-        const u32x4_t pw = {pk[kc][t][0], pk[kc][t][1], pk[kc][t][2], pk[kc][t][3]};
-        oacc[dt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[i], as_bf16x8(pw), oacc[dt][t], 0, 0, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    pv_tile<G, QT>(oacc, pk, st + v_lane);
   };
 
   // Main loop over a ring of NST K/V stages: tile it sits in stage it % NST
@@ -503,6 +535,226 @@ fwd_kernel(const FwdParams p) {
   }
 }
 
+// ------------------------------------------------- key-split workgroup kernel
+// All KW waves of a workgroup own the same 16*QT packed rows and split the
+// workgroup's key range between them: wave w takes key tiles w, w+KW, ...
+// Each wave streams its own K and V tiles into its own LDS buffers (one K
+// and one V buffer: the next K tile is loaded during the softmax and PV of
+// the current one, the next V tile during the next QK^T), so the main loop
+// has no workgroup barrier.  At the end the KW partial results (O, m, l) are
+// merged in wave order through LDS.  Compared with fwd_kernel (waves own
+// different rows and share tiles), a workgroup covers KW times fewer rows, so
+// a small number of rows still fills the chip, while each wave keeps 16*QT
+// rows against every K/V byte it reads from LDS.
+template <int D, int QT, int KW, int BN, bool CAUSAL, bool SPLIT>
+__global__ void __launch_bounds__(KW * 64, 1)
+fwd_ks_kernel(const FwdParams p) {
+  using G = Geo<D, QT, 1, BN>;  // per-wave geometry: one wave issues its own tile copies
+  constexpr int ROWS = 16 * QT;
+  static_assert(!G::TRASH, "per-wave tiles must be whole 64-slot windows");
+  constexpr int OSTR = D * 4 + 16;                       // merge area: bytes per O row (padded)
+  constexpr int MERGE_B = KW * ROWS * OSTR + KW * ROWS * 8;
+  constexpr int LDS_B = KW * G::STAGE_B > MERGE_B ? KW * G::STAGE_B : MERGE_B;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[LDS_B];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int bh = blockIdx.y;
+  const int b = bh / p.Hkv, hk = bh - b * p.Hkv;
+  const int g = p.g;
+
+  int nvalid = p.Sk;
+  if (p.seqused != nullptr) nvalid = min(max(p.seqused[b], 0), p.Sk);
+  nvalid = __builtin_amdgcn_readfirstlane(nvalid);
+
+  RowBlock blk;
+  if constexpr (CAUSAL) {
+    const int nrb = (p.Mp + ROWS - 1) / ROWS;
+    int item = blockIdx.x, rb = nrb - 1;
+    for (; rb >= 0; --rb) {
+      const int kmax = (min((rb + 1) * ROWS, p.Mp) - 1) / g + 1;
+      const int nz = SPLIT ? (kmax + p.kps - 1) / p.kps : 1;
+      if (item < nz) break;
+      item -= nz;
+    }
+    blk.rb = rb;
+    blk.z = item;
+    const int kmax = (min((rb + 1) * ROWS, p.Mp) - 1) / g + 1;
+    blk.kbeg = SPLIT ? item * p.kps : 0;
+    blk.kend = SPLIT ? min(blk.kbeg + p.kps, kmax) : kmax;
+    blk.kend = min(blk.kend, nvalid);
+  } else {
+    blk.rb = blockIdx.x;
+    blk.z = SPLIT ? blockIdx.z : 0;
+    blk.kbeg = SPLIT ? blk.z * p.kps : 0;
+    blk.kend = SPLIT ? min(blk.kbeg + p.kps, nvalid) : nvalid;
+  }
+  const int row0 = blk.rb * ROWS;
+  const int kbeg = blk.kbeg, kend = blk.kend;
+  const int s_lo = min(row0, p.Mp - 1) / g;
+
+  bf16x8_t qf[QT][G::KC];
+  int srow[QT];
+  f32x4_t oacc[G::DT][QT];
+#pragma unroll
+  for (int i = 0; i < G::DT; ++i)
+#pragma unroll
+    for (int t = 0; t < QT; ++t) oacc[i][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run[QT], l_run[QT];
+#pragma unroll
+  for (int t = 0; t < QT; ++t) {
+    m_run[t] = -INFINITY;
+    l_run[t] = 0.f;
+  }
+  const float c2 = p.scale_log2;
+
+  // ---- this wave's K/V copies (see fwd_kernel: out-of-range keys read as 0)
+  const uint32_t rstride_b = (uint32_t)(p.Hkv * D * 2);
+  const size_t kv_base = ((size_t)b * p.Sk * p.Hkv + hk) * D;
+  const uint32_t kv_range = (uint32_t)kend * rstride_b;
+  const u32x4_t rk = make_rsrc(p.k + kv_base, kv_range);
+  const u32x4_t rv = make_rsrc(p.v + kv_base, kv_range);
+  uint32_t voff_k[G::LPT_K], voff_v[G::LPT_V];
+#pragma unroll
+  for (int j = 0; j < G::LPT_K; ++j) {
+    const int P = j * 64 + lane;
+    const int row = P / (G::KSTR / 16), ch = P - row * (G::KSTR / 16);
+    voff_k[j] = (ch < G::CPR) ? row * rstride_b + ch * 16 : kOutOfRange;
+  }
+#pragma unroll
+  for (int j = 0; j < G::LPT_V; ++j) {
+    const int P = j * 64 + lane;
+    const int row = P / (G::VSTR / 16), ch = P - row * (G::VSTR / 16);
+    voff_v[j] = (ch < G::CPR) ? row * rstride_b + ch * 16 : kOutOfRange;
+  }
+  uint8_t* kbuf = smem + wave * G::STAGE_B;
+  uint8_t* vbuf = kbuf + G::K_B;
+  const uint32_t lds_k = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)kbuf);
+  const uint32_t lds_v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)vbuf);
+  // A buffer is refilled only after this wave's reads of it have returned.
+  auto issue_k = [&](int kt) __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    const uint32_t toff = (uint32_t)kt * rstride_b;
+#pragma unroll
+    for (int j = 0; j < G::LPT_K; ++j) copy16_to_lds(rk, voff_k[j] + toff, lds_k + j * 1024);
+  };
+  auto issue_v = [&](int kt) __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    const uint32_t toff = (uint32_t)kt * rstride_b;
+#pragma unroll
+    for (int j = 0; j < G::LPT_V; ++j) copy16_to_lds(rv, voff_v[j] + toff, lds_v + j * 1024);
+  };
+
+  const int ntiles = kend > kbeg ? (kend - kbeg + BN - 1) / BN : 0;
+  const int nown = ntiles > wave ? (ntiles - wave + KW - 1) / KW : 0;  // this wave's tiles
+  if (nown > 0) {
+    issue_k(kbeg + wave * BN);
+    issue_v(kbeg + wave * BN);
+  }
+  // Q^T fragments, loaded after the first copies are on their way.
+#pragma unroll
+  for (int t = 0; t < QT; ++t) {
+    const int r = row0 + 16 * t + col;
+    const bool ok = r < p.Mp;
+    const int s = ok ? r / g : 0;
+    const int hh = ok ? r - s * g : 0;
+    srow[t] = ok ? s : -1;
+    const uint16_t* qp = p.q + ((size_t)(b * p.Sq + s) * p.Hq + hk * g + hh) * D;
+#pragma unroll
+    for (int c = 0; c < G::KC; ++c) {
+      const int d0 = 32 * c + 8 * grp;
+      u32x4_t x = {0u, 0u, 0u, 0u};
+      if (ok && d0 < D) x = ldg16(qp + d0);
+      qf[t][c] = as_bf16x8(x);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // Q and the first K/V tile
+
+  uint32_t k_lane, v_lane;
+  lane_bases<G>(lane, k_lane, v_lane);
+  for (int i = 0; i < nown; ++i) {
+    const int kt = kbeg + (wave + i * KW) * BN;
+    const bool next = i + 1 < nown;
+    if (i > 0) __builtin_amdgcn_s_waitcnt(waitcnt_vm(G::LPT_V));  // K(kt) landed; V(kt) may be in flight
+    f32x4_t sacc[G::MT][QT];
+    uint32_t pk[G::KVC][QT][4];
+    qk_tile<G, QT>(sacc, qf, kbuf + k_lane, grp);
+    if (next) issue_k(kt + KW * BN);  // the K buffer is free once the QK^T reads returned
+    softmax_tile<G, QT, CAUSAL>(sacc, pk, m_run, l_run, oacc, srow, kt, kend, s_lo, c2, grp);
+    __builtin_amdgcn_sched_barrier(0);
+    if (next)
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(G::LPT_K));  // V(kt) landed; the next K may be in flight
+    else
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    pv_tile<G, QT>(oacc, pk, kbuf + v_lane);  // v_lane already includes the K area
+    if (next) issue_v(kt + KW * BN);
+  }
+
+  // ---- merge the KW partials in wave order through LDS
+  float l_tot[QT];
+#pragma unroll
+  for (int t = 0; t < QT; ++t) l_tot[t] = group_sum(l_run[t]);
+  __syncthreads();  // every wave is done with its tiles: the LDS becomes the merge area
+  uint8_t* ob = smem + wave * ROWS * OSTR;
+  float* ml = reinterpret_cast<float*>(smem + KW * ROWS * OSTR) + wave * ROWS * 2;
+#pragma unroll
+  for (int t = 0; t < QT; ++t) {
+    const int rl = 16 * t + col;
+#pragma unroll
+    for (int dt = 0; dt < G::DT; ++dt) {
+      const int d = 16 * dt + 4 * grp;
+      if (d < D) *reinterpret_cast<f32x4_t*>(ob + rl * OSTR + d * 4) = oacc[dt][t];
+    }
+    if (grp == 0) {
+      ml[2 * rl] = m_run[t];
+      ml[2 * rl + 1] = l_tot[t];
+    }
+  }
+  __syncthreads();
+  const float* mls = reinterpret_cast<const float*>(smem + KW * ROWS * OSTR);
+  for (int i = tid; i < ROWS * G::CPR; i += KW * 64) {
+    const int rl = i / G::CPR, ch = i - rl * G::CPR;
+    const int r = row0 + rl;
+    if (r >= p.Mp) continue;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < KW; ++w)
+      if (mls[w * ROWS * 2 + 2 * rl + 1] > 0.f) M = fmaxf(M, mls[w * ROWS * 2 + 2 * rl]);
+    float L = 0.f;
+    f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < KW; ++w) {
+      const float lw = mls[w * ROWS * 2 + 2 * rl + 1];
+      if (!(lw > 0.f)) continue;
+      const float sc = __builtin_amdgcn_exp2f(mls[w * ROWS * 2 + 2 * rl] - M);
+      L += lw * sc;
+      const uint8_t* src = smem + (w * ROWS + rl) * OSTR + ch * 32;
+      a0 += sc * *reinterpret_cast<const f32x4_t*>(src);
+      a1 += sc * *reinterpret_cast<const f32x4_t*>(src + 16);
+    }
+    const float inv = (L > 0.f) ? 1.0f / L : 0.f;
+    const int s = r / g, hh = r - s * g;
+    if constexpr (!SPLIT) {
+      const u32x4_t o = {pack_bf16x2(a0[0] * inv, a0[1] * inv), pack_bf16x2(a0[2] * inv, a0[3] * inv),
+                         pack_bf16x2(a1[0] * inv, a1[1] * inv), pack_bf16x2(a1[2] * inv, a1[3] * inv)};
+      *reinterpret_cast<u32x4_t*>(p.out + ((size_t)(b * p.Sq + s) * p.Hq + hk * g + hh) * D + 8 * ch) = o;
+      if (ch == 0 && p.lse != nullptr) {
+        const float lse = (L > 0.f) ? (M + __log2f(L)) * kLn2 : -INFINITY;
+        p.lse[((size_t)b * p.Hq + hk * g + hh) * p.Sq + s] = lse;
+      }
+    } else {
+      const size_t prow = (((size_t)bh * p.nrb + blk.rb) * p.zmax + blk.z) * ROWS + rl;
+      float* po = p.ws_o + prow * D + 8 * ch;
+      *reinterpret_cast<f32x4_t*>(po) = a0 * inv;
+      *reinterpret_cast<f32x4_t*>(po + 4) = a1 * inv;
+      if (ch == 0) *reinterpret_cast<u32x2_t*>(p.ws_ml + 2 * prow) = u32x2_t{__float_as_uint(M), __float_as_uint(L)};
+    }
+  }
+}
+
 // Merge of the split-KV partials of one packed row and 8 head-dim elements
 // per thread, in split order (deterministic):
 //   M = max_z m_z over non-empty splits, w_z = l_z 2^(m_z - M),
@@ -596,6 +848,38 @@ static hipError_t launch_variant(const FwdParams& p, const LaunchPlan& plan, hip
   return hipGetLastError();
 }
 
+template <int D, int QT, int KW, int BN, bool CAUSAL, bool SPLIT>
+static hipError_t launch_ks_variant(const FwdParams& p, const LaunchPlan& plan, hipStream_t stream) {
+  constexpr int ROWS = 16 * QT;
+  const int nrb = (p.Mp + ROWS - 1) / ROWS;
+  dim3 grid;
+  if (CAUSAL) {
+    int items = 0;
+    for (int rb = 0; rb < nrb; ++rb) {
+      const int kmax = (std::min((rb + 1) * ROWS, p.Mp) - 1) / p.g + 1;
+      items += SPLIT ? (kmax + p.kps - 1) / p.kps : 1;
+    }
+    grid = dim3(items, p.B * p.Hkv, 1);
+  } else {
+    grid = dim3(nrb, p.B * p.Hkv, SPLIT ? plan.nsplit : 1);
+  }
+  hipLaunchKernelGGL((fwd_ks_kernel<D, QT, KW, BN, CAUSAL, SPLIT>), grid, dim3(KW * 64), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !SPLIT) return e;
+  const long long threads = (long long)p.B * p.Hkv * nrb * ROWS * (D / 8);
+  hipLaunchKernelGGL((combine_kernel<D, ROWS, CAUSAL>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                     stream, p);
+  return hipGetLastError();
+}
+
+// Key-split variants (fwd_ks_kernel): head dim, rows per wave / 16, waves
+// (all on the same rows), keys per tile.
+#define FA_KS_VARIANTS(X) \
+  X(64, 2, 4, 64)         \
+  X(72, 2, 4, 64)         \
+  X(256, 2, 4, 32)        \
+  X(256, 2, 2, 32)
+
 // The compiled variants.  Each entry: head dim, rows per wave / 16, waves,
 // keys per tile, K/V stages in LDS.  Every variant is built with and without
 // causal masking and with and without the split-KV partial output.
@@ -607,19 +891,41 @@ static hipError_t launch_variant(const FwdParams& p, const LaunchPlan& plan, hip
   X(72, 2, 4, 64, 2)   \
   X(256, 1, 4, 32, 2)  \
   X(256, 1, 4, 32, 4)  \
+  X(256, 1, 4, 64, 2)  \
   X(256, 2, 4, 32, 2)  \
   X(256, 2, 4, 32, 4)  \
   X(256, 2, 4, 64, 2)
 
-bool variant_exists(int D, int qt, int nw, int bn, int nst) {
+bool variant_exists(int D, int qt, int nw, int kw, int bn, int nst) {
+  if (kw <= 1) {
 #define FA_MATCH(d_, q_, n_, b_, s_) \
   if (D == d_ && qt == q_ && nw == n_ && bn == b_ && nst == s_) return true;
-  FA_VARIANTS(FA_MATCH)
+    FA_VARIANTS(FA_MATCH)
 #undef FA_MATCH
+    return false;
+  }
+  if (nw != kw || nst != 1) return false;
+#define FA_KS_MATCH(d_, q_, k_, b_) \
+  if (D == d_ && qt == q_ && kw == k_ && bn == b_) return true;
+  FA_KS_VARIANTS(FA_KS_MATCH)
+#undef FA_KS_MATCH
   return false;
 }
 
 hipError_t launch_fwd(const FwdParams& p, const LaunchPlan& plan, hipStream_t stream) {
+  if (plan.kw > 1) {
+#define FA_KS_DISPATCH(d_, q_, k_, b_)                                                           \
+  if (plan.D == d_ && plan.qt == q_ && plan.kw == k_ && plan.bn == b_) {                          \
+    if (plan.causal)                                                                             \
+      return plan.split ? launch_ks_variant<d_, q_, k_, b_, true, true>(p, plan, stream)         \
+                        : launch_ks_variant<d_, q_, k_, b_, true, false>(p, plan, stream);       \
+    return plan.split ? launch_ks_variant<d_, q_, k_, b_, false, true>(p, plan, stream)          \
+                      : launch_ks_variant<d_, q_, k_, b_, false, false>(p, plan, stream);        \
+  }
+    FA_KS_VARIANTS(FA_KS_DISPATCH)
+#undef FA_KS_DISPATCH
+    return hipErrorInvalidValue;
+  }
 #define FA_DISPATCH(d_, q_, n_, b_, s_)                                                          \
   if (plan.D == d_ && plan.qt == q_ && plan.nw == n_ && plan.bn == b_ && plan.nst == s_) {        \
     if (plan.causal)                                                                             \

@@ -32,6 +32,7 @@ struct LaunchPlan {
   int D;
   int qt;                  // rows per wave / 16
   int nw;                  // waves per workgroup
+  int kw;                  // waves that split the keys of the same rows (1: waves own different rows)
   int bn;                  // keys per tile
   int nst;                 // K/V tile stages in LDS
   bool causal;
@@ -39,7 +40,7 @@ struct LaunchPlan {
   int nsplit;              // non-causal split count (grid.z)
 };
 
-bool variant_exists(int D, int qt, int nw, int bn, int nst);
+bool variant_exists(int D, int qt, int nw, int kw, int bn, int nst);
 hipError_t launch_fwd(const FwdParams& p, const LaunchPlan& plan, hipStream_t stream);
 
 }  // namespace fa

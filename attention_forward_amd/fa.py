@@ -65,11 +65,11 @@ def load_library():
         lib.fa_set_workspace.argtypes = [vp, ctypes.c_size_t]
         lib.fa_fwd_variant.restype = i32
         lib.fa_fwd_variant.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, f32,
-                                       i32, i32, i32, i32, i32, vp]
+                                       i32, i32, i32, i32, i32, i32, vp]
         lib.fa_fwd_variant_workspace_bytes.restype = ctypes.c_size_t
-        lib.fa_fwd_variant_workspace_bytes.argtypes = [i32] * 12
+        lib.fa_fwd_variant_workspace_bytes.argtypes = [i32] * 13
         lib.fa_fwd_plan.restype = i32
-        lib.fa_fwd_plan.argtypes = [i32] * 7 + [ctypes.POINTER(i32)] * 5
+        lib.fa_fwd_plan.argtypes = [i32] * 7 + [ctypes.POINTER(i32)] * 6
         lib.fa_status_string.restype = ctypes.c_char_p
         lib.fa_status_string.argtypes = [i32]
         lib.fa_abi_version.restype = i32
@@ -92,21 +92,21 @@ def fa_fwd_workspace_bytes(B, Sq, Sk, Hq, Hkv, D, causal) -> int:
 
 
 def fa_fwd_variant(q, k, v, out, lse, B, Sq, Sk, Hq, Hkv, D, causal, seqused_k, scale,
-                   qt, nw, bn, nst, kps, stream) -> int:
+                   qt, nw, kw, bn, nst, kps, stream) -> int:
     """C ``fa_fwd_variant``: fa_fwd with an explicit kernel variant."""
     return load_library().fa_fwd_variant(q or None, k or None, v or None, out or None, lse or None,
                                          B, Sq, Sk, Hq, Hkv, D, int(causal), seqused_k or None,
-                                         ctypes.c_float(scale), qt, nw, bn, nst, kps, stream or None)
+                                         ctypes.c_float(scale), qt, nw, kw, bn, nst, kps, stream or None)
 
 
-def fa_fwd_variant_workspace_bytes(B, Sq, Sk, Hq, Hkv, D, causal, qt, nw, bn, nst, kps) -> int:
+def fa_fwd_variant_workspace_bytes(B, Sq, Sk, Hq, Hkv, D, causal, qt, nw, kw, bn, nst, kps) -> int:
     return int(load_library().fa_fwd_variant_workspace_bytes(B, Sq, Sk, Hq, Hkv, D, int(causal),
-                                                             qt, nw, bn, nst, kps))
+                                                             qt, nw, kw, bn, nst, kps))
 
 
 def fa_fwd_plan(B, Sq, Sk, Hq, Hkv, D, causal):
-    """(qt, nw, bn, nst, kps) that fa_fwd uses for this shape."""
-    out = [ctypes.c_int() for _ in range(5)]
+    """(qt, nw, kw, bn, nst, kps) that fa_fwd uses for this shape."""
+    out = [ctypes.c_int() for _ in range(6)]
     rc = load_library().fa_fwd_plan(B, Sq, Sk, Hq, Hkv, D, int(causal), *[ctypes.byref(x) for x in out])
     if rc != FA_OK:
         raise FAError(rc, "fa_fwd_plan")
@@ -155,8 +155,9 @@ def attention(q, k, v, *, causal=False, seqused_k=None, scale=None, out=None, ls
     q [B, Sq, Hq, D]; k, v [B, Sk, Hkv, D]; seqused_k int32 [B] on the same
     device or None.  ``scale`` defaults to 1/sqrt(D).  Returns (out, lse)
     with lse [B, Hq, Sq] float32 (None when ``return_lse`` is False and no
-    ``lse`` tensor is passed).  ``variant`` = (qt, nw, bn, nst, kps) runs
-    that kernel variant through fa_fwd_variant instead of fa_fwd's choice.
+    ``lse`` tensor is passed).  ``variant`` = (qt, nw, kw, bn, nst, kps)
+    runs that kernel variant through fa_fwd_variant instead of fa_fwd's
+    choice.
     """
     import torch
 
@@ -197,11 +198,8 @@ def attention(q, k, v, *, causal=False, seqused_k=None, scale=None, out=None, ls
             rc = fa_fwd(*ptrs, B, Sq, Sk, Hq, Hkv, D, causal, sq, float(scale), stream)
             where = "fa_fwd"
         else:
-            qt, nw, bn, nst, kps = variant
-            ensure_workspace(dev, fa_fwd_variant_workspace_bytes(B, Sq, Sk, Hq, Hkv, D, causal,
-                                                                 qt, nw, bn, nst, kps))
-            rc = fa_fwd_variant(*ptrs, B, Sq, Sk, Hq, Hkv, D, causal, sq, float(scale), qt, nw, bn, nst, kps,
-                                stream)
+            ensure_workspace(dev, fa_fwd_variant_workspace_bytes(B, Sq, Sk, Hq, Hkv, D, causal, *variant))
+            rc = fa_fwd_variant(*ptrs, B, Sq, Sk, Hq, Hkv, D, causal, sq, float(scale), *variant, stream)
             where = "fa_fwd_variant"
     if rc != FA_OK:
         raise FAError(rc, where)

@@ -102,26 +102,29 @@ int fa_set_workspace(void* dev_ptr, size_t bytes);
 /* Tuning and testing entry points.  fa_fwd picks its kernel variant from
  * the shape alone; these name one explicitly so that every compiled variant
  * can be timed and checked:
- *   qt   rows per wavefront / 16  (1 or 2)
- *   nw   wavefronts per workgroup (4)
- *   bn   keys per tile            (32 or 64)
- *   nst  K/V tile stages in LDS   (2 or 4)
- *   kps  keys per split-KV range  (0: single pass; else a multiple of bn)
+ *   qt   rows per wavefront / 16   (1 or 2)
+ *   nw   wavefronts per workgroup  (2 or 4)
+ *   kw   1: the wavefronts own different rows and share the K/V tiles;
+ *        nw: all wavefronts own the same rows and split the keys between
+ *        them (nst must then be 1: each wavefront streams its own tiles)
+ *   bn   keys per tile             (32 or 64)
+ *   nst  K/V tile stages in LDS    (1, 2 or 4)
+ *   kps  keys per split-KV range   (0: single pass; else a multiple of bn)
  * A combination that is not compiled returns FA_ERR_UNSUPPORTED.  Other
  * arguments, checks and errors are those of fa_fwd. */
 int fa_fwd_variant(const void* q, const void* k, const void* v, void* out, float* lse,
                    int B, int Sq, int Sk, int Hq, int Hkv, int D, int causal,
-                   const int32_t* seqused_k, float scale, int qt, int nw, int bn, int nst, int kps,
-                   hipStream_t stream);
+                   const int32_t* seqused_k, float scale, int qt, int nw, int kw, int bn, int nst,
+                   int kps, hipStream_t stream);
 
 /* Workspace bytes for fa_fwd_variant with that variant (0: none or invalid). */
 size_t fa_fwd_variant_workspace_bytes(int B, int Sq, int Sk, int Hq, int Hkv, int D, int causal,
-                                      int qt, int nw, int bn, int nst, int kps);
+                                      int qt, int nw, int kw, int bn, int nst, int kps);
 
-/* The variant fa_fwd chooses for a shape, written to *qt, *nw, *bn, *nst,
- * *kps.  Returns FA_OK or the shape error fa_fwd would return. */
+/* The variant fa_fwd chooses for a shape, written to *qt, *nw, *kw, *bn,
+ * *nst, *kps.  Returns FA_OK or the shape error fa_fwd would return. */
 int fa_fwd_plan(int B, int Sq, int Sk, int Hq, int Hkv, int D, int causal,
-                int* qt, int* nw, int* bn, int* nst, int* kps);
+                int* qt, int* nw, int* kw, int* bn, int* nst, int* kps);
 
 /* Static, NUL-terminated description of a status code. */
 const char* fa_status_string(int code);

@@ -104,30 +104,45 @@ def test_workspace_sizes(lib):
     # a single-pass plan needs none; a split plan needs some
     for shape in [(1, 1024, 1024, 8, 1, 256, 0), (1, 2048, 2048, 8, 1, 256, 1), (1, 64, 64, 1, 1, 64, 0),
                   (3, 256, 256, 16, 16, 72, 0)]:
-        assert (fa.fa_fwd_workspace_bytes(*shape) > 0) == (fa.fa_fwd_plan(*shape)[4] > 0)
+        assert (fa.fa_fwd_workspace_bytes(*shape) > 0) == (fa.fa_fwd_plan(*shape)[5] > 0)
     assert fa.fa_fwd_workspace_bytes(1, 64, 64, 1, 1, 64, 0) == 0
     assert fa.fa_fwd_workspace_bytes(0, 64, 64, 1, 1, 64, 0) == 0
 
 
 def test_plan_and_variant_sizes(lib):
-    assert fa.fa_fwd_plan(1, 41, 1056, 8, 1, 256, 0)[4] > 0      # small M: split keys
-    assert fa.fa_fwd_plan(3, 256, 256, 16, 16, 72, 0)[4] == 0    # enough rows: single pass
-    qt, nw, bn, nst, kps = fa.fa_fwd_plan(1, 41, 1056, 8, 1, 256, 0)
-    assert fa.fa_fwd_variant_workspace_bytes(1, 41, 1056, 8, 1, 256, 0, qt, nw, bn, nst, kps) == \
+    assert fa.fa_fwd_plan(1, 41, 1056, 8, 1, 256, 0)[5] > 0      # small M: split keys
+    assert fa.fa_fwd_plan(3, 256, 256, 16, 16, 72, 0)[5] == 0    # enough rows: single pass
+    plan = fa.fa_fwd_plan(1, 41, 1056, 8, 1, 256, 0)
+    assert fa.fa_fwd_variant_workspace_bytes(1, 41, 1056, 8, 1, 256, 0, *plan) == \
         fa.fa_fwd_workspace_bytes(1, 41, 1056, 8, 1, 256, 0)
-    assert fa.fa_fwd_variant_workspace_bytes(1, 41, 1056, 8, 1, 256, 0, 3, 4, 64, 2, 0) == 0
-    assert fa.fa_fwd_variant_workspace_bytes(1, 41, 1056, 8, 1, 256, 0, 1, 4, 32, 2, 0) == 0
+    assert fa.fa_fwd_variant_workspace_bytes(1, 41, 1056, 8, 1, 256, 0, 3, 4, 1, 64, 2, 0) == 0
+    assert fa.fa_fwd_variant_workspace_bytes(1, 41, 1056, 8, 1, 256, 0, 1, 4, 1, 32, 2, 0) == 0
+
+
+def test_plan_kernel_choice(lib):
+    # Head dim 256 with at least one 32-row block per compute unit: key-split
+    # workgroups (four waves over the keys of the same rows), no split-KV ...
+    assert fa.fa_fwd_plan(1, 1024, 1024, 8, 1, 256, 0) == (2, 4, 4, 32, 1, 0)
+    assert fa.fa_fwd_plan(1, 2048, 2048, 8, 1, 256, 1) == (2, 4, 4, 32, 1, 0)
+    # ... a padded K/V buffer runs the same plan as the unpadded keys
+    assert fa.fa_fwd_plan(1, 1024, 968, 8, 1, 256, 0) == fa.fa_fwd_plan(1, 1024, 1024, 8, 1, 256, 0)
+    # ... fewer rows, or a smaller head dim: row-split workgroups
+    assert fa.fa_fwd_plan(1, 41, 1056, 8, 1, 256, 0)[:5] == (1, 4, 1, 32, 2)
+    assert fa.fa_fwd_plan(3, 256, 256, 16, 16, 72, 0) == (1, 4, 1, 64, 2, 0)
+    assert fa.fa_fwd_plan(1, 512, 512, 8, 1, 256, 0)[2] == 1      # 128 row blocks of 32
 
 
 def test_variant_rejections(lib):
     args = [Q, K, V, O, L, 1, 64, 64, 8, 1, 256, 0, 0, 0.0625]
-    assert fa.fa_fwd_variant(*args, 3, 4, 64, 2, 0, 0) == fa.FA_ERR_UNSUPPORTED   # not compiled
-    assert fa.fa_fwd_variant(*args, 1, 4, 32, 3, 0, 0) == fa.FA_ERR_UNSUPPORTED   # no 3-stage build
-    assert fa.fa_fwd_variant(*args, 1, 4, 32, 2, 48, 0) == fa.FA_ERR_UNSUPPORTED  # kps % bn
-    assert fa.fa_fwd_variant(*args, 1, 4, 32, 2, -32, 0) == fa.FA_ERR_UNSUPPORTED
+    assert fa.fa_fwd_variant(*args, 3, 4, 1, 64, 2, 0, 0) == fa.FA_ERR_UNSUPPORTED   # not compiled
+    assert fa.fa_fwd_variant(*args, 1, 4, 1, 32, 3, 0, 0) == fa.FA_ERR_UNSUPPORTED   # no 3-stage build
+    assert fa.fa_fwd_variant(*args, 2, 4, 4, 32, 2, 0, 0) == fa.FA_ERR_UNSUPPORTED   # key-split: nst 1
+    assert fa.fa_fwd_variant(*args, 2, 4, 2, 32, 1, 0, 0) == fa.FA_ERR_UNSUPPORTED   # key-split: kw == nw
+    assert fa.fa_fwd_variant(*args, 1, 4, 1, 32, 2, 48, 0) == fa.FA_ERR_UNSUPPORTED  # kps % bn
+    assert fa.fa_fwd_variant(*args, 1, 4, 1, 32, 2, -32, 0) == fa.FA_ERR_UNSUPPORTED
     bad = list(args)
     bad[0] = 0
-    assert fa.fa_fwd_variant(*bad, 1, 4, 32, 2, 0, 0) == fa.FA_ERR_NULL
+    assert fa.fa_fwd_variant(*bad, 1, 4, 1, 32, 2, 0, 0) == fa.FA_ERR_NULL
 
 
 def test_set_workspace_null_with_size(lib):

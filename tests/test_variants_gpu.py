@@ -15,9 +15,13 @@ from tests.gpu_util import assert_parity, run_oracle
 
 pytestmark = pytest.mark.gpu
 
-# (D, qt, nw, bn, nst): the variants compiled into the library
-VARIANTS = [(64, 1, 4, 64, 2), (64, 2, 4, 64, 2), (72, 1, 4, 64, 2), (72, 1, 4, 64, 4), (72, 2, 4, 64, 2),
-            (256, 1, 4, 32, 2), (256, 1, 4, 32, 4), (256, 2, 4, 32, 2), (256, 2, 4, 32, 4), (256, 2, 4, 64, 2)]
+# (D, qt, nw, kw, bn, nst): the variants compiled into the library.  kw = 1:
+# waves own different rows and share K/V tiles; kw = nw: waves share rows and
+# split the keys (each streams its own tiles, nst = 1).
+VARIANTS = [(64, 1, 4, 1, 64, 2), (64, 2, 4, 1, 64, 2), (72, 1, 4, 1, 64, 2), (72, 1, 4, 1, 64, 4),
+            (72, 2, 4, 1, 64, 2), (256, 1, 4, 1, 32, 2), (256, 1, 4, 1, 32, 4), (256, 1, 4, 1, 64, 2),
+            (256, 2, 4, 1, 32, 2), (256, 2, 4, 1, 32, 4), (256, 2, 4, 1, 64, 2),
+            (64, 2, 4, 4, 64, 1), (72, 2, 4, 4, 64, 1), (256, 2, 4, 4, 32, 1), (256, 2, 2, 2, 32, 1)]
 
 SHAPES = {
     # D: (non-causal: B, Sq, Sk, Hq, Hkv, n_valid), (causal: B, S, Hq, Hkv)
@@ -40,7 +44,7 @@ def _run(q, k, v, s, causal, variant, scale):
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("split", [0, 1, 3])
 def test_variant_matches_oracle(gpu_device, var, causal, split):
-    D, qt, nw, bn, nst = var
+    D, qt, nw, kw, bn, nst = var
     kps = split * bn
     print(f"variant {var} causal={causal} kps={kps}", flush=True)
     if causal:
@@ -50,7 +54,7 @@ def test_variant_matches_oracle(gpu_device, var, causal, split):
         B, Sq, Sk, Hq, Hkv, nv = SHAPES[D][0]
         q, k, v, s = make_custom(B, Sq, Sk, Hq, Hkv, D, seed=9 + split, n_valid=nv)
     scale = 1.0 / math.sqrt(D)
-    got = _run(q, k, v, s, causal, (qt, nw, bn, nst, kps), scale)
+    got = _run(q, k, v, s, causal, (qt, nw, kw, bn, nst, kps), scale)
     want = run_oracle(q, k, v, s, causal=causal, scale=scale)
     assert_parity(got, want, f"{var} causal={causal} kps={kps}", strict=False)
 
@@ -60,12 +64,12 @@ def test_variant_matches_oracle(gpu_device, var, causal, split):
 def test_variant_padding_bit_identical(gpu_device, var, split):
     """Same variant, padded buffer + seqused_k vs buffer cut to the valid
     length: bit-identical for every variant, split or not."""
-    D, qt, nw, bn, nst = var
+    D, qt, nw, kw, bn, nst = var
     kps = split * bn
     print(f"padding variant {var} kps={kps}", flush=True)
     q, k, v, s = make_custom(1, 37, 200, 8, 1, D, seed=3, n_valid=131, pad_value=float("nan"))
-    a = _run(q, k, v, s, False, (qt, nw, bn, nst, kps), 0.1)
-    b = _run(q, k[:, :131].contiguous(), v[:, :131].contiguous(), None, False, (qt, nw, bn, nst, kps), 0.1)
+    a = _run(q, k, v, s, False, (qt, nw, kw, bn, nst, kps), 0.1)
+    b = _run(q, k[:, :131].contiguous(), v[:, :131].contiguous(), None, False, (qt, nw, kw, bn, nst, kps), 0.1)
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
@@ -73,8 +77,8 @@ def test_unknown_variant_is_rejected(gpu_device):
     from attention_forward_amd import fa
     q, k, v, _ = make_custom(1, 8, 8, 1, 1, 64, seed=1)
     with pytest.raises(fa.FAError) as e:
-        _run(q, k, v, None, False, (3, 4, 64, 2, 0), 0.125)
+        _run(q, k, v, None, False, (3, 4, 1, 64, 2, 0), 0.125)
     assert e.value.code == fa.FA_ERR_UNSUPPORTED
     with pytest.raises(fa.FAError) as e:
-        _run(q, k, v, None, False, (1, 4, 64, 2, 32), 0.125)  # kps not a multiple of bn
+        _run(q, k, v, None, False, (1, 4, 1, 64, 2, 32), 0.125)  # kps not a multiple of bn
     assert e.value.code == fa.FA_ERR_UNSUPPORTED
