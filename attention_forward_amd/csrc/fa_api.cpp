@@ -77,12 +77,14 @@ void finish_plan(Plan& pl, int B, int Sq, int Sk, int Hq, int Hkv, int causal) {
 }
 
 // Default variant for a shape: a function of the shape only (never of the
-// seqused_k values), so equal shapes always run the same kernel.  Head dim
-// 256 with at least 32 rows per compute unit runs the key-split kernel;
-// otherwise one wave per 16 packed rows.  When the single-pass grid is at most half the compute
-// units, the key range is split into fixed-size ranges, merged afterwards by
-// the combine kernel.  The range size depends on the grid size only, not on
-// the key buffer length, so a padded buffer and the same keys without the
+// seqused_k values), so equal shapes always run the same kernel.
+//  * Head dim 256: key-split workgroups (32 rows, four waves over the keys),
+//    which read half the LDS bytes per MFMA of the row-split kernel.
+//  * Smaller head dims: row-split workgroups, one wave per 16 packed rows.
+// When the single-pass grid is at most half the compute units (non-causal),
+// the key range is split into fixed-size ranges, merged afterwards by the
+// combine kernel.  The range size depends on the grid size only, not on the
+// key buffer length, so a padded buffer and the same keys without the
 // padding are split at the same boundaries (the extra ranges of the padded
 // one are empty and skipped by the merge): their results are bit-identical.
 Plan default_plan(int B, int Sq, int Sk, int Hq, int Hkv, int D, int causal) {
@@ -90,21 +92,18 @@ Plan default_plan(int B, int Sq, int Sk, int Hq, int Hkv, int D, int causal) {
   pl.launch.D = D;
   const long long BH = (long long)B * Hkv;
   const long long Mp = (long long)Sq * (Hq / Hkv);
-  pl.launch.qt = 1;
-  pl.launch.nw = 4;
-  pl.launch.kw = 1;
-  pl.launch.bn = D == 256 ? 32 : 64;
-  pl.launch.nst = 2;
-  if (D == 256 && cdiv(Mp, 32) * BH >= kTargetWorkgroups) {
-    // Enough rows for one key-split workgroup (32 rows, four waves over the
-    // keys) per compute unit: twice the rows per wave of the row-split
-    // kernel, so half the LDS reads per MFMA.
+  if (D == 256) {
     pl.launch.qt = 2;
+    pl.launch.nw = 4;
     pl.launch.kw = 4;
+    pl.launch.bn = 32;
     pl.launch.nst = 1;
-    pl.kps = 0;
-    finish_plan(pl, B, Sq, Sk, Hq, Hkv, causal);
-    return pl;
+  } else {
+    pl.launch.qt = 1;
+    pl.launch.nw = 4;
+    pl.launch.kw = 1;
+    pl.launch.bn = 64;
+    pl.launch.nst = 2;
   }
   const int rows = rows_per_block(pl.launch);
   const long long base = cdiv(Mp, rows) * BH;

@@ -132,10 +132,13 @@ template <int D, int QT, int NW, int BN>
 struct Geo {
   static constexpr int CPR = D / 8;              // 16-byte chunks per K/V row
   static constexpr int ROWB = D * 2;             // bytes per K/V row
-  // LDS row strides: K rows 16 bytes apart modulo 128 (16 rows read with
-  // 16-byte loads hit distinct banks), V rows 32 bytes apart modulo 128 (the
-  // transpose reads take 32 contiguous bytes from each of 4 rows).
-  static constexpr int KSTR = (ROWB % 128 == 0) ? ROWB + 16 : ROWB;
+  // LDS row strides.  A K row holds the head dim rounded up to the 32-element
+  // MFMA step (the rounding is filled with zeros by the tile copies, so the
+  // last step of S^T = K Q^T needs no per-lane guard) plus 16 bytes: an odd
+  // multiple of 16 bytes, so 16 rows read at one column with 16-byte loads
+  // hit distinct banks.  V rows are 32 bytes apart modulo 128 (the transpose
+  // reads take 32 contiguous bytes from each of 4 rows).
+  static constexpr int KSTR = round_up(D, 32) * 2 + 16;
   static constexpr int VSTR = v_stride(ROWB);
   static constexpr int NT = NW * 64;             // threads
   static constexpr int K_SLOTS = round_up(BN * (KSTR / 16), 64);  // 16-byte slots per K tile
@@ -179,9 +182,6 @@ template <class G, int QT>
 __device__ __forceinline__ void qk_tile(f32x4_t (&sacc)[G::MT][QT], const bf16x8_t (&qf)[QT][G::KC],
                                         const uint8_t* kb, int grp) {
   auto load_k = [&](int c, int mt) __attribute__((always_inline)) -> bf16x8_t {
-    if constexpr (4 * (G::KC - 1) + 3 >= G::CPR) {  // head dim not a multiple of 32 (D = 72)
-      if (4 * c + grp >= G::CPR) return as_bf16x8(u32x4_t{0u, 0u, 0u, 0u});
-    }
     return as_bf16x8(*reinterpret_cast<const u32x4_t*>(kb + mt * 16 * G::KSTR + c * 64));
   };
   constexpr int PFK = G::KC < 3 ? G::KC : 3;
@@ -228,30 +228,37 @@ __device__ __forceinline__ bf16x8_t load_v(const uint8_t* vb, int kc, int dt) {
 // commutes with it): p = exp2(s * scale*log2e - m) in one fma + exp.  Keys
 // at or past kend, and for causal keys past the row's position, get p = 0.
 // Updates m_run / l_run, rescales O lazily, and packs P^T to bf16.
+// The mask is needed only where the tile crosses the end of the key range or
+// (causal) the diagonal of the wave's first row.  It is applied in a real
+// branch (the scheduling barrier inside cannot be speculated), so full tiles
+// run no per-element compare and select.
 template <class G, int QT, bool CAUSAL>
 __device__ __forceinline__ void softmax_tile(f32x4_t (&sacc)[G::MT][QT], uint32_t (&pk)[G::KVC][QT][4],
                                              float (&m_run)[QT], float (&l_run)[QT],
                                              f32x4_t (&oacc)[G::DT][QT], const int (&srow)[QT], int kt, int kend,
                                              int s_lo, float c2, int grp) {
   constexpr int BN = G::MT * 16;
-  const bool need_mask = (kt + BN > kend) || (CAUSAL && kt + BN - 1 > s_lo);
+  if ((kt + BN > kend) || (CAUSAL && kt + BN - 1 > s_lo)) {
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < QT; ++t) {
+      // Element (mt, r) of this lane is key kt + 4grp + 16mt + r; it is kept
+      // while 16mt + r is below the lane's limit.
+      int lim = kend - kt - 4 * grp;
+      if constexpr (CAUSAL) lim = min(lim, srow[t] + 1 - kt - 4 * grp);
+#pragma unroll
+      for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sacc[mt][t][r] = (16 * mt + r < lim) ? sacc[mt][t][r] : -INFINITY;
+    }
+  }
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
     float mx = -INFINITY;
 #pragma unroll
     for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float x = sacc[mt][t][r];
-        if (need_mask) {
-          const int key = kt + 16 * mt + 4 * grp + r;
-          bool ok = key < kend;
-          if constexpr (CAUSAL) ok = ok && key <= srow[t];
-          x = ok ? x : -INFINITY;
-          sacc[mt][t][r] = x;
-        }
-        mx = fmaxf(mx, x);
-      }
+      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[mt][t][r]);
     mx = group_max(mx) * c2;
     const float m_new = fmaxf(m_run[t], mx);
     if (__ballot(m_new > m_run[t] + kRescaleThreshold) != 0) {
@@ -321,7 +328,8 @@ fwd_kernel(const FwdParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t trash[G::TRASH ? NW * 1024 : 16];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: wave-level addresses stay scalar
   const int col = lane & 15, grp = lane >> 4;
   const int bh = blockIdx.y;
   const int b = bh / p.Hkv, hk = bh - b * p.Hkv;
@@ -552,13 +560,21 @@ fwd_ks_kernel(const FwdParams p) {
   using G = Geo<D, QT, 1, BN>;  // per-wave geometry: one wave issues its own tile copies
   constexpr int ROWS = 16 * QT;
   static_assert(!G::TRASH, "per-wave tiles must be whole 64-slot windows");
+  // LDS: KW per-wave K/V buffers, then the workgroup's Q tile (rows at the K
+  // stride, read like K fragments); after the main loop the same memory is
+  // the merge area.
+  constexpr int Q_INSTR = round_up(ROWS * (G::KSTR / 16), 64) / 64;  // 1 KiB copies of the Q tile
+  constexpr int Q_OFF = KW * G::STAGE_B;
   constexpr int OSTR = D * 4 + 16;                       // merge area: bytes per O row (padded)
   constexpr int MERGE_B = KW * ROWS * OSTR + KW * ROWS * 8;
-  constexpr int LDS_B = KW * G::STAGE_B > MERGE_B ? KW * G::STAGE_B : MERGE_B;
+  constexpr int TILE_B = Q_OFF + Q_INSTR * 1024;
+  constexpr int LDS_B = TILE_B > MERGE_B ? TILE_B : MERGE_B;
+  static_assert(LDS_B <= 160 * 1024, "LDS of one workgroup");
   __shared__ __attribute__((aligned(16))) uint8_t smem[LDS_B];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: wave-level addresses stay scalar
   const int col = lane & 15, grp = lane >> 4;
   const int bh = blockIdx.y;
   const int b = bh / p.Hkv, hk = bh - b * p.Hkv;
@@ -650,28 +666,53 @@ fwd_ks_kernel(const FwdParams p) {
 
   const int ntiles = kend > kbeg ? (kend - kbeg + BN - 1) / BN : 0;
   const int nown = ntiles > wave ? (ntiles - wave + KW - 1) / KW : 0;  // this wave's tiles
+
+  // Q tile: packed rows row0 .. row0+ROWS-1, copied once per workgroup
+  // (wave w issues copies w, w+KW, ...) into LDS at the K row stride.  The
+  // buffer starts at the block's first position; rows past Mp and the row
+  // padding read as zeros.
+  {
+    const int s_first = row0 / g;
+    const int s_last = (min(row0 + ROWS, p.Mp) - 1) / g;
+    const uint32_t qrow_b = (uint32_t)(p.Hq * D * 2);
+    const u32x4_t rq = make_rsrc(p.q + ((size_t)(b * p.Sq + s_first) * p.Hq + hk * g) * D,
+                                 (uint32_t)(s_last - s_first) * qrow_b + (uint32_t)(g * D * 2));
+    const uint32_t lds_q = (uint32_t)(uintptr_t)(lds_void_t*)(smem + Q_OFF);
+    for (int j = wave; j < Q_INSTR; j += KW) {
+      const int P = j * 64 + lane;
+      const int row = P / (G::KSTR / 16), ch = P - row * (G::KSTR / 16);
+      const int r = row0 + row;
+      uint32_t off = kOutOfRange;
+      if (row < ROWS && ch < G::CPR && r < p.Mp) {
+        const int sq = r / g;
+        off = (uint32_t)(sq - s_first) * qrow_b + (uint32_t)((r - sq * g) * D * 2 + ch * 16);
+      }
+      copy16_to_lds(rq, off, __builtin_amdgcn_readfirstlane(lds_q + j * 1024));
+    }
+  }
+  // First K and V tiles after Q: waiting for all but the V copies then means
+  // Q and K have landed, and the first QK^T overlaps the V copies.
   if (nown > 0) {
     issue_k(kbeg + wave * BN);
     issue_v(kbeg + wave * BN);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(G::LPT_V));
+  } else {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   }
-  // Q^T fragments, loaded after the first copies are on their way.
+  __syncthreads();  // every wave's part of the Q tile is in LDS
+
+  // Q^T fragments from LDS: lane (col, grp) holds packed row row0 + 16t + col,
+  // head-dim elements 32c + 8grp .. +7 (the row's rounding to 32 elements
+  // holds zeros).
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
     const int r = row0 + 16 * t + col;
-    const bool ok = r < p.Mp;
-    const int s = ok ? r / g : 0;
-    const int hh = ok ? r - s * g : 0;
-    srow[t] = ok ? s : -1;
-    const uint16_t* qp = p.q + ((size_t)(b * p.Sq + s) * p.Hq + hk * g + hh) * D;
+    srow[t] = r < p.Mp ? r / g : -1;
 #pragma unroll
     for (int c = 0; c < G::KC; ++c) {
-      const int d0 = 32 * c + 8 * grp;
-      u32x4_t x = {0u, 0u, 0u, 0u};
-      if (ok && d0 < D) x = ldg16(qp + d0);
-      qf[t][c] = as_bf16x8(x);
+      qf[t][c] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(smem + Q_OFF + (16 * t + col) * G::KSTR + c * 64 + grp * 16));
     }
   }
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // Q and the first K/V tile
 
   uint32_t k_lane, v_lane;
   lane_bases<G>(lane, k_lane, v_lane);
@@ -693,64 +734,85 @@ fwd_ks_kernel(const FwdParams p) {
     if (next) issue_v(kt + KW * BN);
   }
 
-  // ---- merge the KW partials in wave order through LDS
+  // ---- merge the KW partials through LDS.  Wave w stores its O (not yet
+  // divided by l) and (m, l) per row; then TPR threads per row read every
+  // wave's (m, l), form the weights 2^(m_w - M) / L (0 for a wave with no
+  // keys) and sum the KW partials of their 16-byte chunks in wave order.
   float l_tot[QT];
 #pragma unroll
   for (int t = 0; t < QT; ++t) l_tot[t] = group_sum(l_run[t]);
   __syncthreads();  // every wave is done with its tiles: the LDS becomes the merge area
-  uint8_t* ob = smem + wave * ROWS * OSTR;
-  float* ml = reinterpret_cast<float*>(smem + KW * ROWS * OSTR) + wave * ROWS * 2;
+  float* mls = reinterpret_cast<float*>(smem + KW * ROWS * OSTR);  // [row][wave] (m, l)
+  {
+    uint8_t* ob = smem + wave * ROWS * OSTR;
 #pragma unroll
-  for (int t = 0; t < QT; ++t) {
-    const int rl = 16 * t + col;
+    for (int t = 0; t < QT; ++t) {
+      const int rl = 16 * t + col;
 #pragma unroll
-    for (int dt = 0; dt < G::DT; ++dt) {
-      const int d = 16 * dt + 4 * grp;
-      if (d < D) *reinterpret_cast<f32x4_t*>(ob + rl * OSTR + d * 4) = oacc[dt][t];
-    }
-    if (grp == 0) {
-      ml[2 * rl] = m_run[t];
-      ml[2 * rl + 1] = l_tot[t];
+      for (int dt = 0; dt < G::DT; ++dt) {
+        const int d = 16 * dt + 4 * grp;
+        if (d < D) *reinterpret_cast<f32x4_t*>(ob + rl * OSTR + d * 4) = oacc[dt][t];
+      }
+      if (grp == 0) *reinterpret_cast<u32x2_t*>(mls + 2 * (rl * KW + wave)) =
+          u32x2_t{__float_as_uint(m_run[t]), __float_as_uint(l_tot[t])};
     }
   }
   __syncthreads();
-  const float* mls = reinterpret_cast<const float*>(smem + KW * ROWS * OSTR);
-  for (int i = tid; i < ROWS * G::CPR; i += KW * 64) {
-    const int rl = i / G::CPR, ch = i - rl * G::CPR;
-    const int r = row0 + rl;
-    if (r >= p.Mp) continue;
+  constexpr int TPR = KW * 64 / ROWS;  // threads per row
+  static_assert(TPR * ROWS == KW * 64, "whole rows per workgroup pass");
+  const int rl = tid / TPR, c0 = tid - rl * TPR;
+  const int r = row0 + rl;
+  if (r < p.Mp) {
+    float mw[KW], fw[KW];
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < KW; ++w)
-      if (mls[w * ROWS * 2 + 2 * rl + 1] > 0.f) M = fmaxf(M, mls[w * ROWS * 2 + 2 * rl]);
+    for (int w = 0; w < KW; ++w) {
+      mw[w] = mls[2 * (rl * KW + w)];
+      fw[w] = mls[2 * (rl * KW + w) + 1];  // l of wave w
+      if (fw[w] > 0.f) M = fmaxf(M, mw[w]);
+    }
     float L = 0.f;
-    f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int w = 0; w < KW; ++w) {
-      const float lw = mls[w * ROWS * 2 + 2 * rl + 1];
-      if (!(lw > 0.f)) continue;
-      const float sc = __builtin_amdgcn_exp2f(mls[w * ROWS * 2 + 2 * rl] - M);
-      L += lw * sc;
-      const uint8_t* src = smem + (w * ROWS + rl) * OSTR + ch * 32;
-      a0 += sc * *reinterpret_cast<const f32x4_t*>(src);
-      a1 += sc * *reinterpret_cast<const f32x4_t*>(src + 16);
+      const float e = fw[w] > 0.f ? __builtin_amdgcn_exp2f(mw[w] - M) : 0.f;
+      L += fw[w] * e;
+      fw[w] = e;
     }
     const float inv = (L > 0.f) ? 1.0f / L : 0.f;
+#pragma unroll
+    for (int w = 0; w < KW; ++w) fw[w] *= inv;
     const int s = r / g, hh = r - s * g;
-    if constexpr (!SPLIT) {
-      const u32x4_t o = {pack_bf16x2(a0[0] * inv, a0[1] * inv), pack_bf16x2(a0[2] * inv, a0[3] * inv),
-                         pack_bf16x2(a1[0] * inv, a1[1] * inv), pack_bf16x2(a1[2] * inv, a1[3] * inv)};
-      *reinterpret_cast<u32x4_t*>(p.out + ((size_t)(b * p.Sq + s) * p.Hq + hk * g + hh) * D + 8 * ch) = o;
-      if (ch == 0 && p.lse != nullptr) {
-        const float lse = (L > 0.f) ? (M + __log2f(L)) * kLn2 : -INFINITY;
-        p.lse[((size_t)b * p.Hq + hk * g + hh) * p.Sq + s] = lse;
+#pragma unroll
+    for (int j = 0; j < (G::CPR + TPR - 1) / TPR; ++j) {
+      const int ch = c0 + TPR * j;
+      if (ch < G::CPR) {
+        f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < KW; ++w) {
+          const uint8_t* src = smem + (w * ROWS + rl) * OSTR + ch * 32;
+          a0 += fw[w] * *reinterpret_cast<const f32x4_t*>(src);
+          a1 += fw[w] * *reinterpret_cast<const f32x4_t*>(src + 16);
+        }
+        if constexpr (!SPLIT) {
+          const u32x4_t o = {pack_bf16x2(a0[0], a0[1]), pack_bf16x2(a0[2], a0[3]), pack_bf16x2(a1[0], a1[1]),
+                             pack_bf16x2(a1[2], a1[3])};
+          *reinterpret_cast<u32x4_t*>(p.out + ((size_t)(b * p.Sq + s) * p.Hq + hk * g + hh) * D + 8 * ch) = o;
+        } else {
+          const size_t prow = (((size_t)bh * p.nrb + blk.rb) * p.zmax + blk.z) * ROWS + rl;
+          float* po = p.ws_o + prow * D + 8 * ch;
+          *reinterpret_cast<f32x4_t*>(po) = a0;
+          *reinterpret_cast<f32x4_t*>(po + 4) = a1;
+        }
       }
-    } else {
-      const size_t prow = (((size_t)bh * p.nrb + blk.rb) * p.zmax + blk.z) * ROWS + rl;
-      float* po = p.ws_o + prow * D + 8 * ch;
-      *reinterpret_cast<f32x4_t*>(po) = a0 * inv;
-      *reinterpret_cast<f32x4_t*>(po + 4) = a1 * inv;
-      if (ch == 0) *reinterpret_cast<u32x2_t*>(p.ws_ml + 2 * prow) = u32x2_t{__float_as_uint(M), __float_as_uint(L)};
+    }
+    if (c0 == 0) {
+      if constexpr (!SPLIT) {
+        if (p.lse != nullptr)
+          p.lse[((size_t)b * p.Hq + hk * g + hh) * p.Sq + s] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : -INFINITY;
+      } else {
+        const size_t prow = (((size_t)bh * p.nrb + blk.rb) * p.zmax + blk.z) * ROWS + rl;
+        *reinterpret_cast<u32x2_t*>(p.ws_ml + 2 * prow) = u32x2_t{__float_as_uint(M), __float_as_uint(L)};
+      }
     }
   }
 }
@@ -885,9 +947,12 @@ static hipError_t launch_ks_variant(const FwdParams& p, const LaunchPlan& plan, 
 // causal masking and with and without the split-KV partial output.
 #define FA_VARIANTS(X) \
   X(64, 1, 4, 64, 2)   \
+  X(64, 2, 2, 64, 2)   \
   X(64, 2, 4, 64, 2)   \
   X(72, 1, 4, 64, 2)   \
   X(72, 1, 4, 64, 4)   \
+  X(72, 2, 2, 64, 2)   \
+  X(72, 2, 2, 64, 3)   \
   X(72, 2, 4, 64, 2)   \
   X(256, 1, 4, 32, 2)  \
   X(256, 1, 4, 32, 4)  \

@@ -120,16 +120,19 @@ def test_plan_and_variant_sizes(lib):
 
 
 def test_plan_kernel_choice(lib):
-    # Head dim 256 with at least one 32-row block per compute unit: key-split
-    # workgroups (four waves over the keys of the same rows), no split-KV ...
+    # Head dim 256: key-split workgroups (four waves over the keys of the same
+    # 32 rows); with a row block per compute unit there is no split-KV ...
     assert fa.fa_fwd_plan(1, 1024, 1024, 8, 1, 256, 0) == (2, 4, 4, 32, 1, 0)
     assert fa.fa_fwd_plan(1, 2048, 2048, 8, 1, 256, 1) == (2, 4, 4, 32, 1, 0)
     # ... a padded K/V buffer runs the same plan as the unpadded keys
     assert fa.fa_fwd_plan(1, 1024, 968, 8, 1, 256, 0) == fa.fa_fwd_plan(1, 1024, 1024, 8, 1, 256, 0)
-    # ... fewer rows, or a smaller head dim: row-split workgroups
-    assert fa.fa_fwd_plan(1, 41, 1056, 8, 1, 256, 0)[:5] == (1, 4, 1, 32, 2)
+    assert fa.fa_fwd_plan(1, 41, 1009, 8, 1, 256, 0) == fa.fa_fwd_plan(1, 41, 1056, 8, 1, 256, 0)
+    # ... few rows: the keys are split into fixed ranges as well
+    assert fa.fa_fwd_plan(1, 41, 1056, 8, 1, 256, 0) == (2, 4, 4, 32, 1, 128)
+    assert fa.fa_fwd_plan(1, 512, 512, 8, 1, 256, 0) == (2, 4, 4, 32, 1, 0)   # 128 blocks: no split
+    # Smaller head dims: row-split workgroups, 16 rows per wave
     assert fa.fa_fwd_plan(3, 256, 256, 16, 16, 72, 0) == (1, 4, 1, 64, 2, 0)
-    assert fa.fa_fwd_plan(1, 512, 512, 8, 1, 256, 0)[2] == 1      # 128 row blocks of 32
+    assert fa.fa_fwd_plan(1, 64, 64, 1, 1, 64, 0) == (1, 4, 1, 64, 2, 0)
 
 
 def test_variant_rejections(lib):
