@@ -313,6 +313,22 @@ __device__ __forceinline__ void pv_tile(f32x4_t (&oacc)[G::DT][QT], const uint32
   }
 }
 
+// Workgroups are dispatched to the eight XCDs round-robin in linear block
+// order, and each XCD has its own L2.  For a non-causal single-pass grid
+// whose (batch, kv head) count is a multiple of 8, block n is given to
+// (batch*kv head, row block) such that every row block of one (batch, kv
+// head) lands on the same XCD and its K/V is fetched into one L2 only.
+__device__ __forceinline__ void xcd_block(int& bh, int& rb) {
+  bh = blockIdx.y;
+  rb = blockIdx.x;
+  if (gridDim.z == 1 && (gridDim.y & 7) == 0) {
+    const int n = blockIdx.x + gridDim.x * blockIdx.y;  // dispatch order
+    const int slot = n >> 3, grp = slot / gridDim.x;
+    bh = (n & 7) + 8 * grp;
+    rb = slot - grp * gridDim.x;
+  }
+}
+
 struct RowBlock {
   int rb;      // row block index
   int z;       // key chunk (split) index
@@ -331,7 +347,13 @@ fwd_kernel(const FwdParams p) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: wave-level addresses stay scalar
   const int col = lane & 15, grp = lane >> 4;
-  const int bh = blockIdx.y;
+  int bh, rb_x;
+  if constexpr (CAUSAL) {
+    bh = blockIdx.y;
+    rb_x = blockIdx.x;
+  } else {
+    xcd_block(bh, rb_x);
+  }
   const int b = bh / p.Hkv, hk = bh - b * p.Hkv;
   const int g = p.g;
 
@@ -358,7 +380,7 @@ fwd_kernel(const FwdParams p) {
     blk.kend = SPLIT ? min(blk.kbeg + p.kps, kmax) : kmax;
     blk.kend = min(blk.kend, nvalid);
   } else {
-    blk.rb = blockIdx.x;
+    blk.rb = rb_x;
     blk.z = SPLIT ? blockIdx.z : 0;
     blk.kbeg = SPLIT ? blk.z * p.kps : 0;
     blk.kend = SPLIT ? min(blk.kbeg + p.kps, nvalid) : nvalid;

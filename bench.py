@@ -115,23 +115,39 @@ class Runner:
             raise self.fa.FAError(rc, "fa_fwd")
 
 
-def time_graph(fn_launch, steps, warmup, device):
-    """Capture `steps` launches in one graph; time one replay.  Returns
-    (wall seconds between the two synchronisations, event seconds)."""
+def capture(fn_launch, steps, warmup, device):
+    """Run `warmup` eager launches, then capture `steps` launches in one graph
+    (uploaded by one untimed replay)."""
     import torch
+
+    indexed = getattr(fn_launch, "takes_index", False)  # fn(stream, i): launch i of the sequence
+
+    def call(h, i):
+        if indexed:
+            fn_launch(h, i)
+        else:
+            fn_launch(h)
 
     stream = torch.cuda.Stream(device=device)
     with torch.cuda.stream(stream):
-        for _ in range(warmup):
-            fn_launch(stream.cuda_stream)
+        for i in range(warmup):
+            call(stream.cuda_stream, i)
     stream.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=stream):
-        for _ in range(steps):
-            fn_launch(torch.cuda.current_stream().cuda_stream)
+        for i in range(steps):
+            call(torch.cuda.current_stream().cuda_stream, i)
     torch.cuda.synchronize()
     graph.replay()  # first replay uploads the graph; not timed
     torch.cuda.synchronize()
+    return graph
+
+
+def replay_timed(graph, device):
+    """One replay between two synchronisations.  Returns (wall seconds,
+    seconds between HIP events recorded around it on the replay stream)."""
+    import torch
+
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     cur = torch.cuda.current_stream(device)
@@ -143,6 +159,76 @@ def time_graph(fn_launch, steps, warmup, device):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     return wall, e0.elapsed_time(e1) * 1e-3
+
+
+def time_graph(fn_launch, steps, warmup, device):
+    """Capture `steps` launches in one graph; time one replay.  Returns
+    (wall seconds between the two synchronisations, event seconds)."""
+    return replay_timed(capture(fn_launch, steps, warmup, device), device)
+
+
+def replay_stats(fn_launch, launches, replays, device):
+    """p50 / p95 of the per-launch time over `replays` replays of a graph of
+    `launches` back-to-back launches (microseconds)."""
+    import statistics
+
+    g = capture(fn_launch, launches, 3, device)
+    per = sorted(replay_timed(g, device)[1] / launches * 1e6 for _ in range(replays))
+    return {"p50": round(statistics.median(per), 3), "p95": round(per[min(len(per) - 1, int(0.95 * len(per)))], 3),
+            "launches_per_replay": launches, "replays": replays}
+
+
+COLD_BYTES = 600 << 20  # more than twice the 256 MiB last-level (MALL) cache
+
+
+def cold_timing(w, device, replays=5):
+    """Per-launch time with the inputs and outputs rotated over enough copies
+    that every launch reads Q/K/V from HBM (the copies together exceed twice
+    the MALL).  The copies hold the same seeded values; only their addresses
+    differ.  Returns µs per launch (median over replays) and the set count."""
+    import statistics
+    import torch
+
+    r = Runner(w, device)
+    flops, nbytes = algorithmic(w)
+    per_set = sum(t.numel() * t.element_size() for t in (r.q, r.k, r.v, r.out, r.lse))
+    nsets = max(2, min(1024, -(-COLD_BYTES // per_set)))
+    sets = []
+    for _ in range(nsets):
+        q, k, v = r.q.clone(), r.k.clone(), r.v.clone()
+        out, lse = torch.empty_like(r.out), torch.empty_like(r.lse)
+        sets.append((q, k, v, out, lse, (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr())
+                     + r.args[5:]))
+    fa = r.fa
+
+    def launch(h, i):
+        rc = fa.fa_fwd(*sets[i % nsets][5], h)
+        if rc != fa.FA_OK:
+            raise fa.FAError(rc, "fa_fwd")
+    launch.takes_index = True
+    g = capture(launch, nsets, 0, device)
+    per = [replay_timed(g, device)[1] / nsets for _ in range(replays)]
+    us = statistics.median(per) * 1e6
+    del sets, g
+    torch.cuda.empty_cache()
+    return {"us_per_call": round(us, 3), "sets": nsets, "set_bytes": per_set,
+            "hbm_gbs": round(nbytes / us / 1e3, 2), "hbm_frac": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 5),
+            "tflops": round(flops / us / 1e6, 3)}
+
+
+def clocks():
+    """Current GPU clocks as reported by rocm-smi (text), or None."""
+    import subprocess
+
+    for cmd in (["rocm-smi", "--showclocks"], ["amd-smi", "metric", "--clock"]):
+        try:
+            res = subprocess.run(cmd, capture_output=True, text=True, timeout=20)
+        except (OSError, subprocess.SubprocessError):
+            continue
+        if res.returncode == 0 and res.stdout.strip():
+            keep = [ln.strip() for ln in res.stdout.splitlines() if "clk" in ln.lower() or "mhz" in ln.lower()]
+            return {"tool": cmd[0], "lines": keep[:16]}
+    return None
 
 
 def dispatch_floor_us(device, steps=200):
@@ -254,6 +340,8 @@ def main(argv=None):
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-all", action="store_true", help="skip the per-workload table")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the replay statistics and the cold-cache timing (for profiler runs)")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--traffic-probe", type=int, default=0, metavar="REPS",
                     help="only run REPS eager calls plus a calibration copy (for rocprofv3 --pmc)")
@@ -306,18 +394,28 @@ def main(argv=None):
         "device": torch.cuda.get_device_name(device),
     }
     line["dispatch_floor_us"] = round(dispatch_floor_us(device), 3)
+    if not a.no_extra:
+        line["replay_stats_us"] = replay_stats(r.step, 100, 20, device)
+        if bound == "hbm":
+            line["cold"] = cold_timing(w, device)
     if not a.no_all:
         table = {}
         for name in WORKLOAD_ORDER:
             wx = WORKLOADS[name]
             steps = max(50, min(a.steps, 400))
-            _, wl, evx, fx, bx = measure(wx, steps, 5, device)
+            rx, wl, evx, fx, bx = measure(wx, steps, 5, device)
             s = evx / steps
             bnd = binding_roofline(fx, bx)
             re = roofline_entry(bnd, fx, bx, s)
-            table[name] = {"us_per_call": round(s * 1e6, 3), "tflops": round(fx / s / 1e12, 3),
-                           "bound": bnd, "frac": re["frac"], "achieved": re["achieved"], "unit": re["unit"]}
+            st = replay_stats(rx.step, 100, 20, device)
+            table[name] = {"us_per_call": round(s * 1e6, 3), "p50": st["p50"], "p95": st["p95"],
+                           "tflops": round(fx / s / 1e12, 3), "bound": bnd, "frac": re["frac"],
+                           "achieved": re["achieved"], "unit": re["unit"],
+                           "plan": list(rx.fa.fa_fwd_plan(wx.B, wx.Sq, wx.Sk, wx.Hq, wx.Hkv, wx.D, int(wx.causal)))}
+            if bnd == "hbm" and name != "single_head":
+                table[name]["cold"] = cold_timing(wx, device)
         line["all_workloads"] = table
+    line["clocks"] = clocks()
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, budget_s=a.cpu_budget)
     else:

@@ -29,7 +29,7 @@ Sources for each part of the definition:
   expert: "Model Demo: PI0.5 End-to-End VLA Inference", section "Model
   stages".
 
-Readings taken where the pages are silent (each listed in the design doc):
+Readings taken where the pages are silent:
 
 * lse is the natural logarithm of the sum of exp(sigma * q . k) over the
   attended keys (scale included), laid out [B, Hq, Sq].

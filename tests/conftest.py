@@ -15,7 +15,7 @@ def pytest_configure(config):
 
 @pytest.fixture(scope="session")
 def gpu_device():
-    """cuda:0 on a GPU machine; GPU tests fail loudly if the device is absent."""
+    """cuda:0; GPU tests fail loudly if the device is absent."""
     import torch
 
     if not torch.cuda.is_available():
