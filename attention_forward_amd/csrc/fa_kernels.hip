@@ -329,6 +329,136 @@ __device__ __forceinline__ void xcd_block(int& bh, int& rb) {
   }
 }
 
+// ---- straight-line tile phases for the software-pipelined loop
+// S^T = K * Q^T with every K fragment loaded up front and no scheduling
+// barriers, so the compiler may interleave these MFMAs with other work.
+template <class G, int QT>
+__device__ __forceinline__ void qk_flat(f32x4_t (&sacc)[G::MT][QT], const bf16x8_t (&qf)[QT][G::KC],
+                                        const uint8_t* kb) {
+  bf16x8_t kf[G::KC][G::MT];
+#pragma unroll
+  for (int c = 0; c < G::KC; ++c)
+#pragma unroll
+    for (int mt = 0; mt < G::MT; ++mt)
+      kf[c][mt] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(kb + mt * 16 * G::KSTR + c * 64));
+#pragma unroll
+  for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+    for (int t = 0; t < QT; ++t) sacc[mt][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < G::KC; ++c)
+#pragma unroll
+    for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+      for (int t = 0; t < QT; ++t)
+        sacc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[c][mt], qf[t][c], sacc[mt][t], 0, 0, 0);
+}
+
+// The mask of softmax_tile on its own (a real branch, taken only by tiles
+// that cross the end of the key range or a causal diagonal).
+template <class G, int QT, bool CAUSAL>
+__device__ __forceinline__ void mask_tile(f32x4_t (&sacc)[G::MT][QT], const int (&srow)[QT], int kt, int kend,
+                                          int s_lo, int grp) {
+  constexpr int BN = G::MT * 16;
+  if ((kt + BN > kend) || (CAUSAL && kt + BN - 1 > s_lo)) {
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < QT; ++t) {
+      int lim = kend - kt - 4 * grp;
+      if constexpr (CAUSAL) lim = min(lim, srow[t] + 1 - kt - 4 * grp);
+#pragma unroll
+      for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sacc[mt][t][r] = (16 * mt + r < lim) ? sacc[mt][t][r] : -INFINITY;
+    }
+  }
+}
+
+// One step of the software-pipelined loop: S^T of the next tile (K fragments
+// at `kn`) into s_nxt, overlapped with the softmax of the current tile
+// (s_cur, already masked) into pk.  The softmax has no branches: the lazy
+// rescale is decided per row and every row multiplies O and l by its factor
+// (1 when its max did not move).  The work is laid out in three phases
+// separated by scheduling barriers, each pairing a third of the S^T MFMAs
+// with independent VALU work: the row max, then the reductions and the
+// rescale, then the exponentials, sums and bf16 packing.  The MFMAs run on
+// the matrix core while the wave issues the VALU instructions.
+template <class G, int QT>
+__device__ __forceinline__ void pipe_tile(f32x4_t (&s_nxt)[G::MT][QT], f32x4_t (&s_cur)[G::MT][QT],
+                                          const bf16x8_t (&qf)[QT][G::KC], const uint8_t* kn,
+                                          uint32_t (&pk)[G::KVC][QT][4], float (&m_run)[QT], float (&l_run)[QT],
+                                          f32x4_t (&oacc)[G::DT][QT], float c2) {
+  constexpr int C1 = (G::KC + 2) / 3, C2 = (2 * G::KC + 2) / 3;
+  bf16x8_t kf[G::KC][G::MT];
+#pragma unroll
+  for (int c = 0; c < G::KC; ++c)
+#pragma unroll
+    for (int mt = 0; mt < G::MT; ++mt)
+      kf[c][mt] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(kn + mt * 16 * G::KSTR + c * 64));
+#pragma unroll
+  for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+    for (int t = 0; t < QT; ++t) s_nxt[mt][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  auto mfmas = [&](int c0, int c1) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = c0; c < c1; ++c)
+#pragma unroll
+      for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+        for (int t = 0; t < QT; ++t)
+          s_nxt[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[c][mt], qf[t][c], s_nxt[mt][t], 0, 0, 0);
+  };
+  // phase 1: row max
+  float mx[QT];
+#pragma unroll
+  for (int t = 0; t < QT; ++t) {
+    mx[t] = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mx[t] = fmaxf(mx[t], s_cur[mt][t][r]);
+  }
+  mfmas(0, C1);
+  __builtin_amdgcn_sched_barrier(0);
+  // phase 2: reductions across the row's four lanes, running max, rescale
+  float m_neg[QT];
+#pragma unroll
+  for (int t = 0; t < QT; ++t) {
+    const float m_new = fmaxf(m_run[t], group_max(mx[t]) * c2);
+    const bool moved = m_new > m_run[t] + kRescaleThreshold;
+    const float alpha = moved ? __builtin_amdgcn_exp2f(m_run[t] - m_new) : 1.f;  // 0 when m_run = -inf
+    m_run[t] = moved ? m_new : m_run[t];
+    l_run[t] *= alpha;
+#pragma unroll
+    for (int i = 0; i < G::DT; ++i) oacc[i][t] *= alpha;
+    m_neg[t] = (m_run[t] == -INFINITY) ? 0.f : -m_run[t];
+  }
+  mfmas(C1, C2);
+  __builtin_amdgcn_sched_barrier(0);
+  // phase 3: p = exp2(s c2 - m), row sums, P^T packed to bf16
+#pragma unroll
+  for (int t = 0; t < QT; ++t) {
+    float lsum = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[mt][t][r], c2, m_neg[t]));
+        s_cur[mt][t][r] = pv;
+        lsum += pv;
+      }
+    l_run[t] += lsum;
+#pragma unroll
+    for (int kc = 0; kc < G::KVC; ++kc) {
+      pk[kc][t][0] = pack_bf16x2(s_cur[2 * kc][t][0], s_cur[2 * kc][t][1]);
+      pk[kc][t][1] = pack_bf16x2(s_cur[2 * kc][t][2], s_cur[2 * kc][t][3]);
+      pk[kc][t][2] = pack_bf16x2(s_cur[2 * kc + 1][t][0], s_cur[2 * kc + 1][t][1]);
+      pk[kc][t][3] = pack_bf16x2(s_cur[2 * kc + 1][t][2], s_cur[2 * kc + 1][t][3]);
+    }
+  }
+  mfmas(C2, G::KC);
+}
+
 struct RowBlock {
   int rb;      // row block index
   int z;       // key chunk (split) index
@@ -502,16 +632,63 @@ fwd_kernel(const FwdParams p) {
   // landed; the prologue tiles are waited for along with them.
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 
-  constexpr int kAhead = (NST - 2) * G::LPT;  // copies allowed in flight after tile it
-  static_assert(kAhead < 64, "vmcnt holds at most 63");
-  for (int it = 0; it < ntiles; ++it) {
-    if (it + NST - 2 < ntiles)
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(kAhead));  // tile it landed (this thread's copies)
-    else
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));       // near the end: everything landed
-    __syncthreads();                                   // everyone's copies; stage (it-1) % NST is free
-    if (it + NST - 1 < ntiles) issue(it + NST - 1);
-    compute_tile(stage + (it % NST) * G::STAGE_B, kbeg + it * BN);
+  if constexpr (NST == 2) {
+    constexpr int kAhead = (NST - 2) * G::LPT;  // copies allowed in flight after tile it
+    for (int it = 0; it < ntiles; ++it) {
+      if (it + NST - 2 < ntiles)
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(kAhead));  // tile it landed (this thread's copies)
+      else
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));       // near the end: everything landed
+      __syncthreads();                                   // everyone's copies; stage (it-1) % NST is free
+      if (it + NST - 1 < ntiles) issue(it + NST - 1);
+      compute_tile(stage + (it % NST) * G::STAGE_B, kbeg + it * BN);
+    }
+  } else {
+    // Software-pipelined loop (three or more stages).  Iteration it issues the
+    // copies of tile it+NST-1 into the stage tile it-1 used, then computes
+    // S^T of tile it+1 in the same straight-line block as the softmax of
+    // tile it (the MFMAs run while the wave issues the softmax VALU work),
+    // then O^T += V^T P^T of tile it.  Before the next iteration tile it+2
+    // must have landed (its S^T comes next) and every wave must be done
+    // with stage it.
+    constexpr int kAhead = (NST - 3) * G::LPT;  // copies allowed in flight after tile it+2
+    static_assert(kAhead < 64, "vmcnt holds at most 63");
+    __syncthreads();  // the prologue tiles are visible to every wave
+    f32x4_t s_cur[G::MT][QT];
+    bool act = wave_active && ntiles > 0;
+    if constexpr (CAUSAL) act = act && kbeg <= s_hi;
+    if (act) qk_flat<G, QT>(s_cur, qf, stage + k_lane);
+    // Byte offsets of the stages of tiles it and it+1, rotated explicitly.
+    int off_cur = 0, off_nxt = G::STAGE_B;
+    for (int it = 0; it < ntiles; ++it) {
+      if (it + NST - 1 < ntiles) issue(it + NST - 1);
+      const int kt = kbeg + it * BN;
+      act = wave_active;
+      if constexpr (CAUSAL) act = act && kt <= s_hi;  // tiles above the wave's last row are skipped
+      if (act) {
+        mask_tile<G, QT, CAUSAL>(s_cur, srow, kt, kend, s_lo, grp);
+        __builtin_amdgcn_sched_barrier(0);
+        // S^T of the next tile (past the last tile the stage holds stale
+        // data and the result is never used) overlapped with this tile's
+        // softmax, then O^T += V^T P^T of this tile.
+        f32x4_t s_nxt[G::MT][QT];
+        uint32_t pk[G::KVC][QT][4];
+        pipe_tile<G, QT>(s_nxt, s_cur, qf, stage + off_nxt + k_lane, pk, m_run, l_run, oacc, c2);
+        __builtin_amdgcn_sched_barrier(0);
+        pv_tile<G, QT>(oacc, pk, stage + off_cur + v_lane);
+#pragma unroll
+        for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+          for (int t = 0; t < QT; ++t) s_cur[mt][t] = s_nxt[mt][t];
+      }
+      off_cur = off_nxt;
+      off_nxt = (off_nxt == (NST - 1) * G::STAGE_B) ? 0 : off_nxt + G::STAGE_B;
+      if (it + NST - 1 < ntiles)
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(kAhead));  // tile it+2 landed (this thread's copies)
+      else
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      __syncthreads();  // everyone's copies; stage it is free
+    }
   }
 
   float l_tot[QT];
@@ -965,13 +1142,17 @@ static hipError_t launch_ks_variant(const FwdParams& p, const LaunchPlan& plan, 
   X(256, 2, 2, 32)
 
 // The compiled variants.  Each entry: head dim, rows per wave / 16, waves,
-// keys per tile, K/V stages in LDS.  Every variant is built with and without
-// causal masking and with and without the split-KV partial output.
+// keys per tile, K/V stages in LDS (two: one tile computed while the next
+// loads; three or more: the software-pipelined loop).  Every variant is
+// built with and without causal masking and with and without the split-KV
+// partial output.
 #define FA_VARIANTS(X) \
   X(64, 1, 4, 64, 2)   \
   X(64, 2, 2, 64, 2)   \
   X(64, 2, 4, 64, 2)   \
+  X(64, 1, 4, 64, 3)   \
   X(72, 1, 4, 64, 2)   \
+  X(72, 1, 4, 64, 3)   \
   X(72, 1, 4, 64, 4)   \
   X(72, 2, 2, 64, 2)   \
   X(72, 2, 2, 64, 3)   \
