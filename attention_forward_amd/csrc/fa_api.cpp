@@ -36,6 +36,12 @@ bool supported_d(int D) { return D == 64 || D == 72 || D == 256; }
 
 long long cdiv(long long a, long long b) { return (a + b - 1) / b; }
 
+// Element strides (batch, sequence, head) of one (B, S, H, D) view.
+struct View {
+  long long sb, ss, sh;
+};
+View contiguous(int S, int H, int D) { return View{(long long)S * H * D, (long long)H * D, (long long)D}; }
+
 struct Plan {
   fa::LaunchPlan launch{};
   int Mp = 0;
@@ -158,10 +164,80 @@ int check_args(const void* q, const void* k, const void* v, void* out, float* ls
   return FA_OK;
 }
 
+// Byte range [lo, hi) touched by a (B, S, H, D) view of 16-bit elements.
+void view_span(const void* base, int B, int S, int H, int D, const View& w, uintptr_t& lo, uintptr_t& hi) {
+  lo = (uintptr_t)base;
+  hi = lo + 2 * (uintptr_t)((B - 1) * w.sb + (S - 1) * w.ss + (H - 1) * w.sh + D);
+}
+
+bool spans_overlap(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) { return a0 < b1 && b0 < a1; }
+
+// Every (batch, position, head) row of the view is disjoint from the others:
+// ordered by stride, each dimension of extent > 1 steps past everything the
+// smaller ones span.
+bool rows_disjoint(int B, int S, int H, int D, const View& w) {
+  struct Dim {
+    long long stride, extent;
+  } d[3] = {{w.sb, B}, {w.ss, S}, {w.sh, H}};
+  std::sort(d, d + 3, [](const Dim& x, const Dim& y) { return x.stride < y.stride; });
+  long long span = D;  // elements covered by the inner dimensions
+  for (const Dim& x : d) {
+    if (x.extent == 1) continue;
+    if (x.stride < span) return false;
+    span = x.stride * (x.extent - 1) + span;
+  }
+  return true;
+}
+
+// Checks of fa_fwd_strided (the strided form of check_args).
+int check_strided(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Sq, int Sk,
+                  int Hq, int Hkv, int D, const View& vq, const View& vk, const View& vv, const View& vo,
+                  int dtype, int causal, const int32_t* seqused_k, float scale) {
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return FA_ERR_NULL;
+  if (B < 1 || Sq < 1 || Sk < 1 || Hq < 1 || Hkv < 1 || D < 1 || Hq % Hkv != 0) return FA_ERR_SHAPE;
+  if (causal != 0 && causal != 1) return FA_ERR_SHAPE;
+  if ((long long)B * Hkv > 65535 || (long long)Sq * (Hq / Hkv) > INT32_MAX / 2) return FA_ERR_SHAPE;
+  const View* views[4] = {&vq, &vk, &vv, &vo};
+  for (const View* w : views)
+    if (w->sb < 0 || w->ss < 0 || w->sh < 0) return FA_ERR_SHAPE;
+  // 32-bit offsets inside the kernels: keys of one (batch, kv head) and the
+  // query rows of one batch entry.
+  if ((long long)Sk * vk.ss * 2 >= (1ll << 31) || (long long)Sk * vv.ss * 2 >= (1ll << 31)) return FA_ERR_SHAPE;
+  if (((long long)(Sq - 1) * vq.ss + (long long)(Hq - 1) * vq.sh + D) * 2 >= (1ll << 31)) return FA_ERR_SHAPE;
+  if (!supported_d(D)) return FA_ERR_UNSUPPORTED;
+  if (dtype != fa::kBf16 && dtype != fa::kF16) return FA_ERR_UNSUPPORTED;
+  if (causal && (Sq != Sk || seqused_k != nullptr)) return FA_ERR_UNSUPPORTED;
+  if (!(scale > 0.0f) || !isfinite(scale)) return FA_ERR_SCALE;
+  // Key rows of one head may not overlap (a row ends before the next starts),
+  // and every output row is written once.
+  if ((Sk > 1 && (vk.ss < D || vv.ss < D)) || !rows_disjoint(B, Sq, Hq, D, vo)) return FA_ERR_SHAPE;
+  // 16-byte rows: 16-byte aligned bases and strides in multiples of 8 elements.
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return FA_ERR_ALIGN;
+  for (const View* w : views)
+    if (w->sb % 8 != 0 || w->ss % 8 != 0 || w->sh % 8 != 0) return FA_ERR_ALIGN;
+  if ((lse != nullptr && !aligned(lse, 4)) || (seqused_k != nullptr && !aligned(seqused_k, 4)))
+    return FA_ERR_ALIGN;
+  uintptr_t q0, q1, k0, k1, v0, v1, o0, o1;
+  view_span(q, B, Sq, Hq, D, vq, q0, q1);
+  view_span(k, B, Sk, Hkv, D, vk, k0, k1);
+  view_span(v, B, Sk, Hkv, D, vv, v0, v1);
+  view_span(out, B, Sq, Hq, D, vo, o0, o1);
+  if (spans_overlap(o0, o1, q0, q1) || spans_overlap(o0, o1, k0, k1) || spans_overlap(o0, o1, v0, v1))
+    return FA_ERR_ALIAS;
+  if (lse != nullptr) {
+    const uintptr_t l0 = (uintptr_t)lse, l1 = l0 + (uintptr_t)B * Hq * Sq * sizeof(float);
+    if (spans_overlap(l0, l1, q0, q1) || spans_overlap(l0, l1, k0, k1) || spans_overlap(l0, l1, v0, v1) ||
+        spans_overlap(l0, l1, o0, o1))
+      return FA_ERR_ALIAS;
+  }
+  return FA_OK;
+}
+
 // Variant given by the caller: checked against the compiled set.
 int variant_plan(Plan& pl, int B, int Sq, int Sk, int Hq, int Hkv, int D, int causal, int qt, int nw, int kw,
                  int bn, int nst, int kps) {
-  if (!fa::variant_exists(D, qt, nw, kw, bn, nst)) return FA_ERR_UNSUPPORTED;
+  if (!fa::variant_exists(D, qt, nw, kw, bn, nst, fa::kBf16)) return FA_ERR_UNSUPPORTED;
+  pl.launch.dtype = fa::kBf16;
   if (kps < 0 || (kps > 0 && kps % bn != 0)) return FA_ERR_UNSUPPORTED;
   pl.launch.D = D;
   pl.launch.qt = qt;
@@ -175,8 +251,8 @@ int variant_plan(Plan& pl, int B, int Sq, int Sk, int Hq, int Hkv, int D, int ca
 }
 
 int run(const Plan& pl, const void* q, const void* k, const void* v, void* out, float* lse, int B, int Sq,
-        int Sk, int Hq, int Hkv, int causal, const int32_t* seqused_k, float scale, hipStream_t stream) {
-  (void)causal;
+        int Sk, int Hq, int Hkv, const View& vq, const View& vk, const View& vv, const View& vo,
+        const int32_t* seqused_k, float scale, hipStream_t stream) {
   fa::FwdParams p{};
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k);
@@ -195,6 +271,10 @@ int run(const Plan& pl, const void* q, const void* k, const void* v, void* out, 
   p.nrb = pl.nrb;
   p.zmax = pl.zmax;
   p.scale_log2 = scale * 1.4426950408889634f;
+  p.q_sb = vq.sb, p.q_ss = vq.ss, p.q_sh = vq.sh;
+  p.k_sb = vk.sb, p.k_ss = vk.ss, p.k_sh = vk.sh;
+  p.v_sb = vv.sb, p.v_ss = vv.ss, p.v_sh = vv.sh;
+  p.o_sb = vo.sb, p.o_ss = vo.ss, p.o_sh = vo.sh;
   if (pl.launch.split) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FA_ERR_LAUNCH;
@@ -224,9 +304,9 @@ const char* fa_status_string(int code) {
   switch (code) {
     case FA_OK: return "FA_OK: success";
     case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
-    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: invalid sizes (need all >= 1, Hq % Hkv == 0, 32-bit element counts)";
-    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: unsupported head_dim (64, 72, 256), kernel variant, or causal with Sq != Sk or with seqused_k";
-    case FA_ERR_ALIGN: return "FA_ERR_ALIGN: q/k/v/out must be 16-byte aligned, lse/seqused_k 4-byte aligned";
+    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: invalid sizes or strides (need all sizes >= 1, Hq % Hkv == 0, offsets within 32 bits, non-negative strides, key rows and output rows that do not overlap)";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: unsupported head_dim (64, 72, 256), element type, kernel variant, or causal with Sq != Sk or with seqused_k";
+    case FA_ERR_ALIGN: return "FA_ERR_ALIGN: q/k/v/out must be 16-byte aligned with strides in multiples of 8 elements, lse/seqused_k 4-byte aligned";
     case FA_ERR_SCALE: return "FA_ERR_SCALE: scale must be finite and > 0";
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: split-KV path needs a registered workspace of fa_fwd_workspace_bytes() bytes";
     case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: the HIP runtime reported an error";
@@ -263,7 +343,24 @@ int fa_fwd(const void* q, const void* k, const void* v, void* out, float* lse, i
   int rc = check_args(q, k, v, out, lse, B, Sq, Sk, Hq, Hkv, D, causal, seqused_k, scale);
   if (rc != FA_OK) return rc;
   const Plan pl = default_plan(B, Sq, Sk, Hq, Hkv, D, causal);
-  return run(pl, q, k, v, out, lse, B, Sq, Sk, Hq, Hkv, causal, seqused_k, scale, stream);
+  return run(pl, q, k, v, out, lse, B, Sq, Sk, Hq, Hkv, contiguous(Sq, Hq, D), contiguous(Sk, Hkv, D),
+             contiguous(Sk, Hkv, D), contiguous(Sq, Hq, D), seqused_k, scale, stream);
+}
+
+int fa_fwd_strided(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Sq, int Sk,
+                   int Hq, int Hkv, int D, int64_t q_sb, int64_t q_ss, int64_t q_sh, int64_t k_sb, int64_t k_ss,
+                   int64_t k_sh, int64_t v_sb, int64_t v_ss, int64_t v_sh, int64_t o_sb, int64_t o_ss,
+                   int64_t o_sh, int dtype, int causal, const int32_t* seqused_k, float scale,
+                   hipStream_t stream) {
+  const View vq{q_sb, q_ss, q_sh}, vk{k_sb, k_ss, k_sh}, vv{v_sb, v_ss, v_sh}, vo{o_sb, o_ss, o_sh};
+  const int rc = check_strided(q, k, v, out, lse, B, Sq, Sk, Hq, Hkv, D, vq, vk, vv, vo, dtype, causal, seqused_k,
+                               scale);
+  if (rc != FA_OK) return rc;
+  Plan pl = default_plan(B, Sq, Sk, Hq, Hkv, D, causal);
+  pl.launch.dtype = dtype;
+  if (!fa::variant_exists(D, pl.launch.qt, pl.launch.nw, pl.launch.kw, pl.launch.bn, pl.launch.nst, dtype))
+    return FA_ERR_UNSUPPORTED;
+  return run(pl, q, k, v, out, lse, B, Sq, Sk, Hq, Hkv, vq, vk, vv, vo, seqused_k, scale, stream);
 }
 
 int fa_fwd_variant(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Sq, int Sk,
@@ -274,7 +371,8 @@ int fa_fwd_variant(const void* q, const void* k, const void* v, void* out, float
   Plan pl;
   rc = variant_plan(pl, B, Sq, Sk, Hq, Hkv, D, causal, qt, nw, kw, bn, nst, kps);
   if (rc != FA_OK) return rc;
-  return run(pl, q, k, v, out, lse, B, Sq, Sk, Hq, Hkv, causal, seqused_k, scale, stream);
+  return run(pl, q, k, v, out, lse, B, Sq, Sk, Hq, Hkv, contiguous(Sq, Hq, D), contiguous(Sk, Hkv, D),
+             contiguous(Sk, Hkv, D), contiguous(Sq, Hq, D), seqused_k, scale, stream);
 }
 
 int fa_fwd_plan(int B, int Sq, int Sk, int Hq, int Hkv, int D, int causal, int* qt, int* nw, int* kw, int* bn,

@@ -54,6 +54,7 @@
 namespace fa {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -74,13 +75,41 @@ constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) 
 constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
 
 __device__ __forceinline__ u32x4_t ldg16(const uint16_t* p) { return *reinterpret_cast<const u32x4_t*>(p); }
-__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t x) { return __builtin_bit_cast(bf16x8_t, x); }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   bf16x2_t r = {(__bf16)lo, (__bf16)hi};  // v_cvt_pk_bf16_f32, round to nearest even
   return __builtin_bit_cast(uint32_t, r);
 }
+
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+  f16x2_t r = {(_Float16)lo, (_Float16)hi};  // round to nearest even
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Element type of q, k, v and out: the MFMA that consumes eight of them per
+// lane, and the rounding of P and of the output.
+template <int DTY>
+struct Elem;
+template <>
+struct Elem<kBf16> {
+  typedef bf16x8_t v8;
+  static __device__ __forceinline__ v8 cast(u32x4_t x) { return __builtin_bit_cast(v8, x); }
+  static __device__ __forceinline__ f32x4_t mfma(v8 a, v8 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack(float lo, float hi) { return pack_bf16x2(lo, hi); }
+};
+template <>
+struct Elem<kF16> {
+  typedef f16x8_t v8;
+  static __device__ __forceinline__ v8 cast(u32x4_t x) { return __builtin_bit_cast(v8, x); }
+  static __device__ __forceinline__ f32x4_t mfma(v8 a, v8 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack(float lo, float hi) { return pack_f16x2(lo, hi); }
+};
 
 // x combined over lanes l, l^16, l^32, l^48 (the four 16-lane rows that hold
 // one accumulator column).  permlane32_swap(x, x) gives {x[l & 31], x[l | 32]}
@@ -128,8 +157,9 @@ constexpr int round_up(int x, int m) { return (x + m - 1) / m * m; }
 constexpr int v_stride(int bytes) { return (bytes % 128 == 32) ? bytes : v_stride(bytes + 16); }
 
 // Compile-time geometry of one kernel variant.
-template <int D, int QT, int NW, int BN>
+template <int D, int QT, int NW, int BN, int DTY = kBf16>
 struct Geo {
+  using E = Elem<DTY>;                           // element type of q, k, v, out
   static constexpr int CPR = D / 8;              // 16-byte chunks per K/V row
   static constexpr int ROWB = D * 2;             // bytes per K/V row
   // LDS row strides.  A K row holds the head dim rounded up to the 32-element
@@ -179,17 +209,17 @@ __device__ __forceinline__ void lane_bases(int lane, uint32_t& k_lane, uint32_t&
 // use them; the scheduling barriers keep that order so LDS latency overlaps
 // MFMA work.
 template <class G, int QT>
-__device__ __forceinline__ void qk_tile(f32x4_t (&sacc)[G::MT][QT], const bf16x8_t (&qf)[QT][G::KC],
+__device__ __forceinline__ void qk_tile(f32x4_t (&sacc)[G::MT][QT], const typename G::E::v8 (&qf)[QT][G::KC],
                                         const uint8_t* kb, int grp) {
-  auto load_k = [&](int c, int mt) __attribute__((always_inline)) -> bf16x8_t {
-    return as_bf16x8(*reinterpret_cast<const u32x4_t*>(kb + mt * 16 * G::KSTR + c * 64));
+  auto load_k = [&](int c, int mt) __attribute__((always_inline)) -> typename G::E::v8 {
+    return G::E::cast(*reinterpret_cast<const u32x4_t*>(kb + mt * 16 * G::KSTR + c * 64));
   };
   constexpr int PFK = G::KC < 3 ? G::KC : 3;
 #pragma unroll
   for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
     for (int t = 0; t < QT; ++t) sacc[mt][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  bf16x8_t kf[G::KC][G::MT];
+  typename G::E::v8 kf[G::KC][G::MT];
 #pragma unroll
   for (int c = 0; c < PFK; ++c)
 #pragma unroll
@@ -205,7 +235,7 @@ __device__ __forceinline__ void qk_tile(f32x4_t (&sacc)[G::MT][QT], const bf16x8
     for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
       for (int t = 0; t < QT; ++t)
-        sacc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[c][mt], qf[t][c], sacc[mt][t], 0, 0, 0);
+        sacc[mt][t] = G::E::mfma(kf[c][mt], qf[t][c], sacc[mt][t]);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -216,12 +246,12 @@ __device__ __forceinline__ void qk_tile(f32x4_t (&sacc)[G::MT][QT], const bf16x8
 // head-dim 16dt + col, i.e. the slots P^T holds in elements 4h .. 4h+3.
 // Past the head dim (D = 72, dt = 4) the reads land in the row padding.
 template <class G>
-__device__ __forceinline__ bf16x8_t load_v(const uint8_t* vb, int kc, int dt) {
+__device__ __forceinline__ typename G::E::v8 load_v(const uint8_t* vb, int kc, int dt) {
   const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vb + (32 * kc) * G::VSTR + dt * 32));
   const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vb + (32 * kc + 16) * G::VSTR + dt * 32));
   const u32x4_t vw = {__builtin_bit_cast(u32x2_t, lo)[0], __builtin_bit_cast(u32x2_t, lo)[1],
                       __builtin_bit_cast(u32x2_t, hi)[0], __builtin_bit_cast(u32x2_t, hi)[1]};
-  return as_bf16x8(vw);
+  return G::E::cast(vw);
 }
 
 // Online softmax of one tile on the raw scores (scale > 0, so the max
@@ -281,10 +311,10 @@ __device__ __forceinline__ void softmax_tile(f32x4_t (&sacc)[G::MT][QT], uint32_
     l_run[t] += lsum;
 #pragma unroll
     for (int kc = 0; kc < G::KVC; ++kc) {
-      pk[kc][t][0] = pack_bf16x2(sacc[2 * kc][t][0], sacc[2 * kc][t][1]);
-      pk[kc][t][1] = pack_bf16x2(sacc[2 * kc][t][2], sacc[2 * kc][t][3]);
-      pk[kc][t][2] = pack_bf16x2(sacc[2 * kc + 1][t][0], sacc[2 * kc + 1][t][1]);
-      pk[kc][t][3] = pack_bf16x2(sacc[2 * kc + 1][t][2], sacc[2 * kc + 1][t][3]);
+      pk[kc][t][0] = G::E::pack(sacc[2 * kc][t][0], sacc[2 * kc][t][1]);
+      pk[kc][t][1] = G::E::pack(sacc[2 * kc][t][2], sacc[2 * kc][t][3]);
+      pk[kc][t][2] = G::E::pack(sacc[2 * kc + 1][t][0], sacc[2 * kc + 1][t][1]);
+      pk[kc][t][3] = G::E::pack(sacc[2 * kc + 1][t][2], sacc[2 * kc + 1][t][3]);
     }
   }
 }
@@ -296,7 +326,7 @@ __device__ __forceinline__ void pv_tile(f32x4_t (&oacc)[G::DT][QT], const uint32
                                         const uint8_t* vb) {
   constexpr int NV = G::KVC * G::DT;
   constexpr int PFV = NV < 4 ? NV : 4;
-  bf16x8_t vf[NV];
+  typename G::E::v8 vf[NV];
 #pragma unroll
   for (int i = 0; i < PFV; ++i) vf[i] = load_v<G>(vb, i / G::DT, i % G::DT);
 #pragma unroll
@@ -307,7 +337,7 @@ __device__ __forceinline__ void pv_tile(f32x4_t (&oacc)[G::DT][QT], const uint32
 #pragma unroll
     for (int t = 0; t < QT; ++t) {
       const u32x4_t pw = {pk[kc][t][0], pk[kc][t][1], pk[kc][t][2], pk[kc][t][3]};
-      oacc[dt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[i], as_bf16x8(pw), oacc[dt][t], 0, 0, 0);
+      oacc[dt][t] = G::E::mfma(vf[i], G::E::cast(pw), oacc[dt][t]);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -333,14 +363,14 @@ __device__ __forceinline__ void xcd_block(int& bh, int& rb) {
 // S^T = K * Q^T with every K fragment loaded up front and no scheduling
 // barriers, so the compiler may interleave these MFMAs with other work.
 template <class G, int QT>
-__device__ __forceinline__ void qk_flat(f32x4_t (&sacc)[G::MT][QT], const bf16x8_t (&qf)[QT][G::KC],
+__device__ __forceinline__ void qk_flat(f32x4_t (&sacc)[G::MT][QT], const typename G::E::v8 (&qf)[QT][G::KC],
                                         const uint8_t* kb) {
-  bf16x8_t kf[G::KC][G::MT];
+  typename G::E::v8 kf[G::KC][G::MT];
 #pragma unroll
   for (int c = 0; c < G::KC; ++c)
 #pragma unroll
     for (int mt = 0; mt < G::MT; ++mt)
-      kf[c][mt] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(kb + mt * 16 * G::KSTR + c * 64));
+      kf[c][mt] = G::E::cast(*reinterpret_cast<const u32x4_t*>(kb + mt * 16 * G::KSTR + c * 64));
 #pragma unroll
   for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
@@ -351,7 +381,7 @@ __device__ __forceinline__ void qk_flat(f32x4_t (&sacc)[G::MT][QT], const bf16x8
     for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
       for (int t = 0; t < QT; ++t)
-        sacc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[c][mt], qf[t][c], sacc[mt][t], 0, 0, 0);
+        sacc[mt][t] = G::E::mfma(kf[c][mt], qf[t][c], sacc[mt][t]);
 }
 
 // The mask of softmax_tile on its own (a real branch, taken only by tiles
@@ -385,16 +415,16 @@ __device__ __forceinline__ void mask_tile(f32x4_t (&sacc)[G::MT][QT], const int 
 // the matrix core while the wave issues the VALU instructions.
 template <class G, int QT>
 __device__ __forceinline__ void pipe_tile(f32x4_t (&s_nxt)[G::MT][QT], f32x4_t (&s_cur)[G::MT][QT],
-                                          const bf16x8_t (&qf)[QT][G::KC], const uint8_t* kn,
+                                          const typename G::E::v8 (&qf)[QT][G::KC], const uint8_t* kn,
                                           uint32_t (&pk)[G::KVC][QT][4], float (&m_run)[QT], float (&l_run)[QT],
                                           f32x4_t (&oacc)[G::DT][QT], float c2) {
   constexpr int C1 = (G::KC + 2) / 3, C2 = (2 * G::KC + 2) / 3;
-  bf16x8_t kf[G::KC][G::MT];
+  typename G::E::v8 kf[G::KC][G::MT];
 #pragma unroll
   for (int c = 0; c < G::KC; ++c)
 #pragma unroll
     for (int mt = 0; mt < G::MT; ++mt)
-      kf[c][mt] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(kn + mt * 16 * G::KSTR + c * 64));
+      kf[c][mt] = G::E::cast(*reinterpret_cast<const u32x4_t*>(kn + mt * 16 * G::KSTR + c * 64));
 #pragma unroll
   for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
@@ -406,7 +436,7 @@ __device__ __forceinline__ void pipe_tile(f32x4_t (&s_nxt)[G::MT][QT], f32x4_t (
       for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
         for (int t = 0; t < QT; ++t)
-          s_nxt[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[c][mt], qf[t][c], s_nxt[mt][t], 0, 0, 0);
+          s_nxt[mt][t] = G::E::mfma(kf[c][mt], qf[t][c], s_nxt[mt][t]);
   };
   // phase 1: row max
   float mx[QT];
@@ -450,10 +480,10 @@ __device__ __forceinline__ void pipe_tile(f32x4_t (&s_nxt)[G::MT][QT], f32x4_t (
     l_run[t] += lsum;
 #pragma unroll
     for (int kc = 0; kc < G::KVC; ++kc) {
-      pk[kc][t][0] = pack_bf16x2(s_cur[2 * kc][t][0], s_cur[2 * kc][t][1]);
-      pk[kc][t][1] = pack_bf16x2(s_cur[2 * kc][t][2], s_cur[2 * kc][t][3]);
-      pk[kc][t][2] = pack_bf16x2(s_cur[2 * kc + 1][t][0], s_cur[2 * kc + 1][t][1]);
-      pk[kc][t][3] = pack_bf16x2(s_cur[2 * kc + 1][t][2], s_cur[2 * kc + 1][t][3]);
+      pk[kc][t][0] = G::E::pack(s_cur[2 * kc][t][0], s_cur[2 * kc][t][1]);
+      pk[kc][t][1] = G::E::pack(s_cur[2 * kc][t][2], s_cur[2 * kc][t][3]);
+      pk[kc][t][2] = G::E::pack(s_cur[2 * kc + 1][t][0], s_cur[2 * kc + 1][t][1]);
+      pk[kc][t][3] = G::E::pack(s_cur[2 * kc + 1][t][2], s_cur[2 * kc + 1][t][3]);
     }
   }
   mfmas(C2, G::KC);
@@ -465,10 +495,10 @@ struct RowBlock {
   int kbeg, kend;
 };
 
-template <int D, int QT, int NW, int BN, int NST, bool CAUSAL, bool SPLIT>
+template <int D, int QT, int NW, int BN, int NST, bool CAUSAL, bool SPLIT, int DTY>
 __global__ void __launch_bounds__(NW * 64, 1)
 fwd_kernel(const FwdParams p) {
-  using G = Geo<D, QT, NW, BN>;
+  using G = Geo<D, QT, NW, BN, DTY>;
   static_assert(NST >= 2, "at least double buffering");
   __shared__ __attribute__((aligned(16))) uint8_t stage[NST * G::STAGE_B];
   __shared__ __attribute__((aligned(16))) uint8_t trash[G::TRASH ? NW * 1024 : 16];
@@ -519,7 +549,7 @@ fwd_kernel(const FwdParams p) {
   const int rw0 = row0 + wave * 16 * QT;
   const int kbeg = blk.kbeg, kend = blk.kend;
 
-  bf16x8_t qf[QT][G::KC];
+  typename G::E::v8 qf[QT][G::KC];
   int srow[QT];
   const bool wave_active = rw0 < p.Mp;
   const int s_lo = min(rw0, p.Mp - 1) / g;
@@ -540,11 +570,9 @@ fwd_kernel(const FwdParams p) {
 
   // ---- K/V tile copies.  Buffers start at this (batch, kv head)'s first key
   // and end after key kend - 1, so every key at or past kend reads as zero.
-  const uint32_t rstride_b = (uint32_t)(p.Hkv * D * 2);  // bytes between consecutive keys
-  const size_t kv_base = ((size_t)b * p.Sk * p.Hkv + hk) * D;
-  const uint32_t kv_range = (uint32_t)kend * rstride_b;
-  const u32x4_t rk = make_rsrc(p.k + kv_base, kv_range);
-  const u32x4_t rv = make_rsrc(p.v + kv_base, kv_range);
+  const uint32_t rstride_k = (uint32_t)(p.k_ss * 2), rstride_v = (uint32_t)(p.v_ss * 2);  // bytes between keys
+  const u32x4_t rk = make_rsrc(p.k + b * p.k_sb + hk * p.k_sh, (uint32_t)kend * rstride_k);
+  const u32x4_t rv = make_rsrc(p.v + b * p.v_sb + hk * p.v_sh, (uint32_t)kend * rstride_v);
   // Per-thread source offsets of its slots within a tile: slot P holds row
   // P / (STR/16), chunk P % (STR/16); padding chunks and trash windows read
   // out of range (zeros, no memory access).
@@ -553,13 +581,13 @@ fwd_kernel(const FwdParams p) {
   for (int j = 0; j < G::LPT_K; ++j) {
     const int P = j * G::NT + tid;
     const int row = P / (G::KSTR / 16), ch = P - row * (G::KSTR / 16);
-    voff_k[j] = (P < G::K_SLOTS && ch < G::CPR) ? row * rstride_b + ch * 16 : kOutOfRange;
+    voff_k[j] = (P < G::K_SLOTS && ch < G::CPR) ? row * rstride_k + ch * 16 : kOutOfRange;
   }
 #pragma unroll
   for (int j = 0; j < G::LPT_V; ++j) {
     const int P = j * G::NT + tid;
     const int row = P / (G::VSTR / 16), ch = P - row * (G::VSTR / 16);
-    voff_v[j] = (P < G::V_SLOTS && ch < G::CPR) ? row * rstride_b + ch * 16 : kOutOfRange;
+    voff_v[j] = (P < G::V_SLOTS && ch < G::CPR) ? row * rstride_v + ch * 16 : kOutOfRange;
   }
   const uint32_t lds_stage0 = (uint32_t)(uintptr_t)(lds_void_t*)stage;
   const uint32_t lds_trash = (uint32_t)(uintptr_t)(lds_void_t*)trash + wave * 1024;
@@ -568,18 +596,19 @@ fwd_kernel(const FwdParams p) {
   // below 2^31 (checked on the host), so adding it to kOutOfRange cannot wrap.
   auto issue = [&](int it) __attribute__((always_inline)) {
     const uint32_t st = lds_stage0 + (it % NST) * G::STAGE_B;
-    const uint32_t toff = (uint32_t)(kbeg + it * BN) * rstride_b;
+    const uint32_t toff_k = (uint32_t)(kbeg + it * BN) * rstride_k;
+    const uint32_t toff_v = (uint32_t)(kbeg + it * BN) * rstride_v;
 #pragma unroll
     for (int j = 0; j < G::LPT_K; ++j) {
       const int pbase = j * G::NT + wave * 64;
       const uint32_t dst = (!G::TRASH || pbase < G::K_SLOTS) ? st + pbase * 16 : lds_trash;
-      copy16_to_lds(rk, voff_k[j] + toff, __builtin_amdgcn_readfirstlane(dst));
+      copy16_to_lds(rk, voff_k[j] + toff_k, __builtin_amdgcn_readfirstlane(dst));
     }
 #pragma unroll
     for (int j = 0; j < G::LPT_V; ++j) {
       const int pbase = j * G::NT + wave * 64;
       const uint32_t dst = (!G::TRASH || pbase < G::V_SLOTS) ? st + G::K_B + pbase * 16 : lds_trash;
-      copy16_to_lds(rv, voff_v[j] + toff, __builtin_amdgcn_readfirstlane(dst));
+      copy16_to_lds(rv, voff_v[j] + toff_v, __builtin_amdgcn_readfirstlane(dst));
     }
   };
 
@@ -619,13 +648,13 @@ fwd_kernel(const FwdParams p) {
     const int s = ok ? r / g : 0;
     const int hh = ok ? r - s * g : 0;
     srow[t] = ok ? s : -1;
-    const uint16_t* qp = p.q + ((size_t)(b * p.Sq + s) * p.Hq + hk * g + hh) * D;
+    const uint16_t* qp = p.q + b * p.q_sb + s * p.q_ss + (hk * g + hh) * p.q_sh;
 #pragma unroll
     for (int c = 0; c < G::KC; ++c) {
       const int d0 = 32 * c + 8 * grp;
       u32x4_t x = {0u, 0u, 0u, 0u};
       if (ok && d0 < D) x = ldg16(qp + d0);
-      qf[t][c] = as_bf16x8(x);
+      qf[t][c] = G::E::cast(x);
     }
   }
   // vmcnt(0) as a builtin, so that the compiler knows the Q fragments have
@@ -704,13 +733,13 @@ fwd_kernel(const FwdParams p) {
       const int s = r / g, hh = r - s * g;
       const float l = l_tot[t];
       const float inv = (l > 0.f) ? 1.0f / l : 0.f;
-      uint16_t* op = p.out + ((size_t)(b * p.Sq + s) * p.Hq + hk * g + hh) * D;
+      uint16_t* op = p.out + b * p.o_sb + s * p.o_ss + (hk * g + hh) * p.o_sh;
 #pragma unroll
       for (int dt = 0; dt < G::DT; ++dt) {
         const int d = 16 * dt + 4 * grp;
         if (d < D) {
-          u32x2_t w = {pack_bf16x2(oacc[dt][t][0] * inv, oacc[dt][t][1] * inv),
-                       pack_bf16x2(oacc[dt][t][2] * inv, oacc[dt][t][3] * inv)};
+          u32x2_t w = {G::E::pack(oacc[dt][t][0] * inv, oacc[dt][t][1] * inv),
+                       G::E::pack(oacc[dt][t][2] * inv, oacc[dt][t][3] * inv)};
           *reinterpret_cast<u32x2_t*>(op + d) = w;
         }
       }
@@ -753,10 +782,10 @@ fwd_kernel(const FwdParams p) {
 // different rows and share tiles), a workgroup covers KW times fewer rows, so
 // a small number of rows still fills the chip, while each wave keeps 16*QT
 // rows against every K/V byte it reads from LDS.
-template <int D, int QT, int KW, int BN, bool CAUSAL, bool SPLIT>
+template <int D, int QT, int KW, int BN, bool CAUSAL, bool SPLIT, int DTY>
 __global__ void __launch_bounds__(KW * 64, 1)
 fwd_ks_kernel(const FwdParams p) {
-  using G = Geo<D, QT, 1, BN>;  // per-wave geometry: one wave issues its own tile copies
+  using G = Geo<D, QT, 1, BN, DTY>;  // per-wave geometry: one wave issues its own tile copies
   constexpr int ROWS = 16 * QT;
   static_assert(!G::TRASH, "per-wave tiles must be whole 64-slot windows");
   // LDS: KW per-wave K/V buffers, then the workgroup's Q tile (rows at the K
@@ -809,7 +838,7 @@ fwd_ks_kernel(const FwdParams p) {
   const int kbeg = blk.kbeg, kend = blk.kend;
   const int s_lo = min(row0, p.Mp - 1) / g;
 
-  bf16x8_t qf[QT][G::KC];
+  typename G::E::v8 qf[QT][G::KC];
   int srow[QT];
   f32x4_t oacc[G::DT][QT];
 #pragma unroll
@@ -825,23 +854,21 @@ fwd_ks_kernel(const FwdParams p) {
   const float c2 = p.scale_log2;
 
   // ---- this wave's K/V copies (see fwd_kernel: out-of-range keys read as 0)
-  const uint32_t rstride_b = (uint32_t)(p.Hkv * D * 2);
-  const size_t kv_base = ((size_t)b * p.Sk * p.Hkv + hk) * D;
-  const uint32_t kv_range = (uint32_t)kend * rstride_b;
-  const u32x4_t rk = make_rsrc(p.k + kv_base, kv_range);
-  const u32x4_t rv = make_rsrc(p.v + kv_base, kv_range);
+  const uint32_t rstride_k = (uint32_t)(p.k_ss * 2), rstride_v = (uint32_t)(p.v_ss * 2);
+  const u32x4_t rk = make_rsrc(p.k + b * p.k_sb + hk * p.k_sh, (uint32_t)kend * rstride_k);
+  const u32x4_t rv = make_rsrc(p.v + b * p.v_sb + hk * p.v_sh, (uint32_t)kend * rstride_v);
   uint32_t voff_k[G::LPT_K], voff_v[G::LPT_V];
 #pragma unroll
   for (int j = 0; j < G::LPT_K; ++j) {
     const int P = j * 64 + lane;
     const int row = P / (G::KSTR / 16), ch = P - row * (G::KSTR / 16);
-    voff_k[j] = (ch < G::CPR) ? row * rstride_b + ch * 16 : kOutOfRange;
+    voff_k[j] = (ch < G::CPR) ? row * rstride_k + ch * 16 : kOutOfRange;
   }
 #pragma unroll
   for (int j = 0; j < G::LPT_V; ++j) {
     const int P = j * 64 + lane;
     const int row = P / (G::VSTR / 16), ch = P - row * (G::VSTR / 16);
-    voff_v[j] = (ch < G::CPR) ? row * rstride_b + ch * 16 : kOutOfRange;
+    voff_v[j] = (ch < G::CPR) ? row * rstride_v + ch * 16 : kOutOfRange;
   }
   uint8_t* kbuf = smem + wave * G::STAGE_B;
   uint8_t* vbuf = kbuf + G::K_B;
@@ -851,14 +878,14 @@ fwd_ks_kernel(const FwdParams p) {
   auto issue_k = [&](int kt) __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    const uint32_t toff = (uint32_t)kt * rstride_b;
+    const uint32_t toff = (uint32_t)kt * rstride_k;
 #pragma unroll
     for (int j = 0; j < G::LPT_K; ++j) copy16_to_lds(rk, voff_k[j] + toff, lds_k + j * 1024);
   };
   auto issue_v = [&](int kt) __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    const uint32_t toff = (uint32_t)kt * rstride_b;
+    const uint32_t toff = (uint32_t)kt * rstride_v;
 #pragma unroll
     for (int j = 0; j < G::LPT_V; ++j) copy16_to_lds(rv, voff_v[j] + toff, lds_v + j * 1024);
   };
@@ -873,9 +900,9 @@ fwd_ks_kernel(const FwdParams p) {
   {
     const int s_first = row0 / g;
     const int s_last = (min(row0 + ROWS, p.Mp) - 1) / g;
-    const uint32_t qrow_b = (uint32_t)(p.Hq * D * 2);
-    const u32x4_t rq = make_rsrc(p.q + ((size_t)(b * p.Sq + s_first) * p.Hq + hk * g) * D,
-                                 (uint32_t)(s_last - s_first) * qrow_b + (uint32_t)(g * D * 2));
+    const uint32_t qrow_b = (uint32_t)(p.q_ss * 2), qhead_b = (uint32_t)(p.q_sh * 2);
+    const u32x4_t rq = make_rsrc(p.q + b * p.q_sb + s_first * p.q_ss + hk * g * p.q_sh,
+                                 (uint32_t)(s_last - s_first) * qrow_b + (uint32_t)(g - 1) * qhead_b + D * 2);
     const uint32_t lds_q = (uint32_t)(uintptr_t)(lds_void_t*)(smem + Q_OFF);
     for (int j = wave; j < Q_INSTR; j += KW) {
       const int P = j * 64 + lane;
@@ -884,7 +911,7 @@ fwd_ks_kernel(const FwdParams p) {
       uint32_t off = kOutOfRange;
       if (row < ROWS && ch < G::CPR && r < p.Mp) {
         const int sq = r / g;
-        off = (uint32_t)(sq - s_first) * qrow_b + (uint32_t)((r - sq * g) * D * 2 + ch * 16);
+        off = (uint32_t)(sq - s_first) * qrow_b + (uint32_t)(r - sq * g) * qhead_b + (uint32_t)(ch * 16);
       }
       copy16_to_lds(rq, off, __builtin_amdgcn_readfirstlane(lds_q + j * 1024));
     }
@@ -909,7 +936,7 @@ fwd_ks_kernel(const FwdParams p) {
     srow[t] = r < p.Mp ? r / g : -1;
 #pragma unroll
     for (int c = 0; c < G::KC; ++c) {
-      qf[t][c] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(smem + Q_OFF + (16 * t + col) * G::KSTR + c * 64 + grp * 16));
+      qf[t][c] = G::E::cast(*reinterpret_cast<const u32x4_t*>(smem + Q_OFF + (16 * t + col) * G::KSTR + c * 64 + grp * 16));
     }
   }
 
@@ -993,9 +1020,9 @@ fwd_ks_kernel(const FwdParams p) {
           a1 += fw[w] * *reinterpret_cast<const f32x4_t*>(src + 16);
         }
         if constexpr (!SPLIT) {
-          const u32x4_t o = {pack_bf16x2(a0[0], a0[1]), pack_bf16x2(a0[2], a0[3]), pack_bf16x2(a1[0], a1[1]),
-                             pack_bf16x2(a1[2], a1[3])};
-          *reinterpret_cast<u32x4_t*>(p.out + ((size_t)(b * p.Sq + s) * p.Hq + hk * g + hh) * D + 8 * ch) = o;
+          const u32x4_t o = {G::E::pack(a0[0], a0[1]), G::E::pack(a0[2], a0[3]), G::E::pack(a1[0], a1[1]),
+                             G::E::pack(a1[2], a1[3])};
+          *reinterpret_cast<u32x4_t*>(p.out + b * p.o_sb + s * p.o_ss + (hk * g + hh) * p.o_sh + 8 * ch) = o;
         } else {
           const size_t prow = (((size_t)bh * p.nrb + blk.rb) * p.zmax + blk.z) * ROWS + rl;
           float* po = p.ws_o + prow * D + 8 * ch;
@@ -1021,9 +1048,10 @@ fwd_ks_kernel(const FwdParams p) {
 //   M = max_z m_z over non-empty splits, w_z = l_z 2^(m_z - M),
 //   out = sum_z w_z Ohat_z / sum_z w_z,   lse = ln2 (M + log2 sum_z w_z).
 // The running form below rescales as M grows, which is the same sum.
-template <int D, int ROWS_WG, bool CAUSAL>
+template <int D, int ROWS_WG, bool CAUSAL, int DTY>
 __global__ void __launch_bounds__(256)
 combine_kernel(const FwdParams p) {
+  using E = Elem<DTY>;
   constexpr int CPR = D / 8;
   const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
   const long long per_bh = (long long)p.nrb * ROWS_WG * CPR;
@@ -1074,9 +1102,9 @@ combine_kernel(const FwdParams p) {
   }
   const int s = r / g, hh = r - s * g;
   const float inv = (L > 0.f) ? 1.0f / L : 0.f;
-  const u32x4_t o = {pack_bf16x2(a0[0] * inv, a0[1] * inv), pack_bf16x2(a0[2] * inv, a0[3] * inv),
-                     pack_bf16x2(a1[0] * inv, a1[1] * inv), pack_bf16x2(a1[2] * inv, a1[3] * inv)};
-  *reinterpret_cast<u32x4_t*>(p.out + ((size_t)(b * p.Sq + s) * p.Hq + hk * g + hh) * D + 8 * ch) = o;
+  const u32x4_t o = {E::pack(a0[0] * inv, a0[1] * inv), E::pack(a0[2] * inv, a0[3] * inv),
+                     E::pack(a1[0] * inv, a1[1] * inv), E::pack(a1[2] * inv, a1[3] * inv)};
+  *reinterpret_cast<u32x4_t*>(p.out + b * p.o_sb + s * p.o_ss + (hk * g + hh) * p.o_sh + 8 * ch) = o;
   if (ch == 0 && p.lse != nullptr) {
     const float lse = (L > 0.f) ? (M + __log2f(L)) * kLn2 : -INFINITY;
     p.lse[((size_t)b * p.Hq + hk * g + hh) * p.Sq + s] = lse;
@@ -1085,9 +1113,9 @@ combine_kernel(const FwdParams p) {
 
 // ------------------------------------------------------------------ launch
 
-template <int D, int QT, int NW, int BN, int NST, bool CAUSAL, bool SPLIT>
+template <int D, int QT, int NW, int BN, int NST, bool CAUSAL, bool SPLIT, int DTY>
 static hipError_t launch_variant(const FwdParams& p, const LaunchPlan& plan, hipStream_t stream) {
-  using G = Geo<D, QT, NW, BN>;
+  using G = Geo<D, QT, NW, BN, DTY>;
   const int nrb = (p.Mp + G::ROWS_WG - 1) / G::ROWS_WG;
   dim3 grid;
   if (CAUSAL) {
@@ -1100,16 +1128,16 @@ static hipError_t launch_variant(const FwdParams& p, const LaunchPlan& plan, hip
   } else {
     grid = dim3(nrb, p.B * p.Hkv, SPLIT ? plan.nsplit : 1);
   }
-  hipLaunchKernelGGL((fwd_kernel<D, QT, NW, BN, NST, CAUSAL, SPLIT>), grid, dim3(NW * 64), 0, stream, p);
+  hipLaunchKernelGGL((fwd_kernel<D, QT, NW, BN, NST, CAUSAL, SPLIT, DTY>), grid, dim3(NW * 64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !SPLIT) return e;
   const long long threads = (long long)p.B * p.Hkv * nrb * G::ROWS_WG * (D / 8);
-  hipLaunchKernelGGL((combine_kernel<D, G::ROWS_WG, CAUSAL>), dim3((unsigned)((threads + 255) / 256)), dim3(256),
-                     0, stream, p);
+  hipLaunchKernelGGL((combine_kernel<D, G::ROWS_WG, CAUSAL, DTY>), dim3((unsigned)((threads + 255) / 256)),
+                     dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
-template <int D, int QT, int KW, int BN, bool CAUSAL, bool SPLIT>
+template <int D, int QT, int KW, int BN, bool CAUSAL, bool SPLIT, int DTY>
 static hipError_t launch_ks_variant(const FwdParams& p, const LaunchPlan& plan, hipStream_t stream) {
   constexpr int ROWS = 16 * QT;
   const int nrb = (p.Mp + ROWS - 1) / ROWS;
@@ -1124,57 +1152,60 @@ static hipError_t launch_ks_variant(const FwdParams& p, const LaunchPlan& plan, 
   } else {
     grid = dim3(nrb, p.B * p.Hkv, SPLIT ? plan.nsplit : 1);
   }
-  hipLaunchKernelGGL((fwd_ks_kernel<D, QT, KW, BN, CAUSAL, SPLIT>), grid, dim3(KW * 64), 0, stream, p);
+  hipLaunchKernelGGL((fwd_ks_kernel<D, QT, KW, BN, CAUSAL, SPLIT, DTY>), grid, dim3(KW * 64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !SPLIT) return e;
   const long long threads = (long long)p.B * p.Hkv * nrb * ROWS * (D / 8);
-  hipLaunchKernelGGL((combine_kernel<D, ROWS, CAUSAL>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+  hipLaunchKernelGGL((combine_kernel<D, ROWS, CAUSAL, DTY>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
                      stream, p);
   return hipGetLastError();
 }
 
-// Key-split variants (fwd_ks_kernel): head dim, rows per wave / 16, waves
-// (all on the same rows), keys per tile.
-#define FA_KS_VARIANTS(X) \
-  X(64, 2, 4, 64)         \
-  X(72, 2, 4, 64)         \
-  X(256, 2, 4, 32)        \
-  X(256, 2, 2, 32)
-
-// The compiled variants.  Each entry: head dim, rows per wave / 16, waves,
-// keys per tile, K/V stages in LDS (two: one tile computed while the next
-// loads; three or more: the software-pipelined loop).  Every variant is
+// The compiled variants.  Row-split (fwd_kernel) entries: element type, head
+// dim, rows per wave / 16, waves, keys per tile, K/V stages in LDS (two: one
+// tile computed while the next loads; three or more: the software-pipelined
+// loop).  Key-split (fwd_ks_kernel) entries: element type, head dim, rows per
+// wave / 16, waves (all on the same rows), keys per tile.  Every variant is
 // built with and without causal masking and with and without the split-KV
-// partial output.
-#define FA_VARIANTS(X) \
-  X(64, 1, 4, 64, 2)   \
-  X(64, 2, 2, 64, 2)   \
-  X(64, 2, 4, 64, 2)   \
-  X(64, 1, 4, 64, 3)   \
-  X(72, 1, 4, 64, 2)   \
-  X(72, 1, 4, 64, 3)   \
-  X(72, 1, 4, 64, 4)   \
-  X(72, 2, 2, 64, 2)   \
-  X(72, 2, 2, 64, 3)   \
-  X(72, 2, 4, 64, 2)   \
-  X(256, 1, 4, 32, 2)  \
-  X(256, 1, 4, 32, 4)  \
-  X(256, 1, 4, 64, 2)  \
-  X(256, 2, 4, 32, 2)  \
-  X(256, 2, 4, 32, 4)  \
-  X(256, 2, 4, 64, 2)
+// partial output.  fp16 has the variants the default plan uses.
+#define FA_VARIANTS(X)        \
+  X(kBf16, 64, 1, 4, 64, 2)   \
+  X(kBf16, 64, 2, 2, 64, 2)   \
+  X(kBf16, 64, 2, 4, 64, 2)   \
+  X(kBf16, 64, 1, 4, 64, 3)   \
+  X(kBf16, 72, 1, 4, 64, 2)   \
+  X(kBf16, 72, 1, 4, 64, 3)   \
+  X(kBf16, 72, 1, 4, 64, 4)   \
+  X(kBf16, 72, 2, 2, 64, 2)   \
+  X(kBf16, 72, 2, 2, 64, 3)   \
+  X(kBf16, 72, 2, 4, 64, 2)   \
+  X(kBf16, 256, 1, 4, 32, 2)  \
+  X(kBf16, 256, 1, 4, 32, 4)  \
+  X(kBf16, 256, 1, 4, 64, 2)  \
+  X(kBf16, 256, 2, 4, 32, 2)  \
+  X(kBf16, 256, 2, 4, 32, 4)  \
+  X(kBf16, 256, 2, 4, 64, 2)  \
+  X(kF16, 64, 1, 4, 64, 2)    \
+  X(kF16, 72, 1, 4, 64, 2)
 
-bool variant_exists(int D, int qt, int nw, int kw, int bn, int nst) {
+#define FA_KS_VARIANTS(X)  \
+  X(kBf16, 64, 2, 4, 64)   \
+  X(kBf16, 72, 2, 4, 64)   \
+  X(kBf16, 256, 2, 4, 32)  \
+  X(kBf16, 256, 2, 2, 32)  \
+  X(kF16, 256, 2, 4, 32)
+
+bool variant_exists(int D, int qt, int nw, int kw, int bn, int nst, int dtype) {
   if (kw <= 1) {
-#define FA_MATCH(d_, q_, n_, b_, s_) \
-  if (D == d_ && qt == q_ && nw == n_ && bn == b_ && nst == s_) return true;
+#define FA_MATCH(t_, d_, q_, n_, b_, s_) \
+  if (dtype == t_ && D == d_ && qt == q_ && nw == n_ && bn == b_ && nst == s_) return true;
     FA_VARIANTS(FA_MATCH)
 #undef FA_MATCH
     return false;
   }
   if (nw != kw || nst != 1) return false;
-#define FA_KS_MATCH(d_, q_, k_, b_) \
-  if (D == d_ && qt == q_ && kw == k_ && bn == b_) return true;
+#define FA_KS_MATCH(t_, d_, q_, k_, b_) \
+  if (dtype == t_ && D == d_ && qt == q_ && kw == k_ && bn == b_) return true;
   FA_KS_VARIANTS(FA_KS_MATCH)
 #undef FA_KS_MATCH
   return false;
@@ -1182,25 +1213,25 @@ bool variant_exists(int D, int qt, int nw, int kw, int bn, int nst) {
 
 hipError_t launch_fwd(const FwdParams& p, const LaunchPlan& plan, hipStream_t stream) {
   if (plan.kw > 1) {
-#define FA_KS_DISPATCH(d_, q_, k_, b_)                                                           \
-  if (plan.D == d_ && plan.qt == q_ && plan.kw == k_ && plan.bn == b_) {                          \
-    if (plan.causal)                                                                             \
-      return plan.split ? launch_ks_variant<d_, q_, k_, b_, true, true>(p, plan, stream)         \
-                        : launch_ks_variant<d_, q_, k_, b_, true, false>(p, plan, stream);       \
-    return plan.split ? launch_ks_variant<d_, q_, k_, b_, false, true>(p, plan, stream)          \
-                      : launch_ks_variant<d_, q_, k_, b_, false, false>(p, plan, stream);        \
+#define FA_KS_DISPATCH(t_, d_, q_, k_, b_)                                                          \
+  if (plan.dtype == t_ && plan.D == d_ && plan.qt == q_ && plan.kw == k_ && plan.bn == b_) {         \
+    if (plan.causal)                                                                                \
+      return plan.split ? launch_ks_variant<d_, q_, k_, b_, true, true, t_>(p, plan, stream)        \
+                        : launch_ks_variant<d_, q_, k_, b_, true, false, t_>(p, plan, stream);      \
+    return plan.split ? launch_ks_variant<d_, q_, k_, b_, false, true, t_>(p, plan, stream)         \
+                      : launch_ks_variant<d_, q_, k_, b_, false, false, t_>(p, plan, stream);       \
   }
     FA_KS_VARIANTS(FA_KS_DISPATCH)
 #undef FA_KS_DISPATCH
     return hipErrorInvalidValue;
   }
-#define FA_DISPATCH(d_, q_, n_, b_, s_)                                                          \
-  if (plan.D == d_ && plan.qt == q_ && plan.nw == n_ && plan.bn == b_ && plan.nst == s_) {        \
-    if (plan.causal)                                                                             \
-      return plan.split ? launch_variant<d_, q_, n_, b_, s_, true, true>(p, plan, stream)        \
-                        : launch_variant<d_, q_, n_, b_, s_, true, false>(p, plan, stream);      \
-    return plan.split ? launch_variant<d_, q_, n_, b_, s_, false, true>(p, plan, stream)         \
-                      : launch_variant<d_, q_, n_, b_, s_, false, false>(p, plan, stream);       \
+#define FA_DISPATCH(t_, d_, q_, n_, b_, s_)                                                               \
+  if (plan.dtype == t_ && plan.D == d_ && plan.qt == q_ && plan.nw == n_ && plan.bn == b_ && plan.nst == s_) { \
+    if (plan.causal)                                                                                     \
+      return plan.split ? launch_variant<d_, q_, n_, b_, s_, true, true, t_>(p, plan, stream)            \
+                        : launch_variant<d_, q_, n_, b_, s_, true, false, t_>(p, plan, stream);          \
+    return plan.split ? launch_variant<d_, q_, n_, b_, s_, false, true, t_>(p, plan, stream)             \
+                      : launch_variant<d_, q_, n_, b_, s_, false, false, t_>(p, plan, stream);           \
   }
   FA_VARIANTS(FA_DISPATCH)
 #undef FA_DISPATCH

@@ -9,11 +9,11 @@ namespace fa {
 
 // Everything a forward launch needs, by value (kernel argument).
 struct FwdParams {
-  const uint16_t* q;       // [B, Sq, Hq, D] bf16
-  const uint16_t* k;       // [B, Sk, Hkv, D] bf16
-  const uint16_t* v;       // [B, Sk, Hkv, D] bf16
-  uint16_t* out;           // [B, Sq, Hq, D] bf16
-  float* lse;              // [B, Hq, Sq] fp32 or null
+  const uint16_t* q;       // (batch, position, head, head_dim) view, 16-bit elements
+  const uint16_t* k;       // (batch, key, kv head, head_dim) view
+  const uint16_t* v;       // (batch, key, kv head, head_dim) view
+  uint16_t* out;           // (batch, position, head, head_dim) view, written
+  float* lse;              // [B, Hq, Sq] fp32 contiguous, or null
   const int32_t* seqused;  // [B] int32 on the device, or null
   // Split-KV workspace (split variants only).  Partial rows are indexed
   // ((bh * nrb + row_block) * zmax + split) * rows_per_block + row_in_block.
@@ -26,7 +26,15 @@ struct FwdParams {
   int nrb;                 // row blocks per (batch, kv head)
   int zmax;                // most splits of any row block
   float scale_log2;        // scale * log2(e)
+  // Element strides of the views (batch, sequence, head); head_dim is
+  // contiguous.  Contiguous BSHD: (S*H*D, H*D, D).
+  long long q_sb, q_ss, q_sh;
+  long long k_sb, k_ss, k_sh;
+  long long v_sb, v_ss, v_sh;
+  long long o_sb, o_ss, o_sh;
 };
+
+enum ElemType { kBf16 = 0, kF16 = 1 };
 
 struct LaunchPlan {
   int D;
@@ -38,9 +46,10 @@ struct LaunchPlan {
   bool causal;
   bool split;
   int nsplit;              // non-causal split count (grid.z)
+  int dtype;               // ElemType of q, k, v and out
 };
 
-bool variant_exists(int D, int qt, int nw, int kw, int bn, int nst);
+bool variant_exists(int D, int qt, int nw, int kw, int bn, int nst, int dtype);
 hipError_t launch_fwd(const FwdParams& p, const LaunchPlan& plan, hipStream_t stream);
 
 }  // namespace fa

@@ -30,7 +30,10 @@ FA_ERR_WORKSPACE = 6
 FA_ERR_LAUNCH = 7
 FA_ERR_ALIAS = 8
 
-EXPORTS = ("fa_fwd", "fa_fwd_workspace_bytes", "fa_set_workspace", "fa_fwd_variant",
+FA_BF16 = 0
+FA_FP16 = 1
+
+EXPORTS = ("fa_fwd", "fa_fwd_strided", "fa_fwd_workspace_bytes", "fa_set_workspace", "fa_fwd_variant",
            "fa_fwd_variant_workspace_bytes", "fa_fwd_plan", "fa_status_string", "fa_abi_version")
 
 _lib = None
@@ -59,6 +62,9 @@ def load_library():
         vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
         lib.fa_fwd.restype = i32
         lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, f32, vp]
+        i64 = ctypes.c_int64
+        lib.fa_fwd_strided.restype = i32
+        lib.fa_fwd_strided.argtypes = [vp, vp, vp, vp, vp] + [i32] * 6 + [i64] * 12 + [i32, i32, vp, f32, vp]
         lib.fa_fwd_workspace_bytes.restype = ctypes.c_size_t
         lib.fa_fwd_workspace_bytes.argtypes = [i32] * 7
         lib.fa_set_workspace.restype = i32
@@ -85,6 +91,17 @@ def fa_fwd(q, k, v, out, lse, B, Sq, Sk, Hq, Hkv, D, causal, seqused_k, scale, s
     return load_library().fa_fwd(q or None, k or None, v or None, out or None, lse or None,
                                  B, Sq, Sk, Hq, Hkv, D, int(causal), seqused_k or None,
                                  ctypes.c_float(scale), stream or None)
+
+
+def fa_fwd_strided(q, k, v, out, lse, B, Sq, Sk, Hq, Hkv, D, q_strides, k_strides, v_strides, o_strides,
+                   dtype, causal, seqused_k, scale, stream) -> int:
+    """C ``fa_fwd_strided``; each ``*_strides`` is (batch, seq, head) in elements."""
+    st = [int(x) for x in (*q_strides, *k_strides, *v_strides, *o_strides)]
+    if len(st) != 12:
+        raise ValueError("each stride triple needs three entries")
+    return load_library().fa_fwd_strided(q or None, k or None, v or None, out or None, lse or None,
+                                         B, Sq, Sk, Hq, Hkv, D, *st, int(dtype), int(causal),
+                                         seqused_k or None, ctypes.c_float(scale), stream or None)
 
 
 def fa_fwd_workspace_bytes(B, Sq, Sk, Hq, Hkv, D, causal) -> int:
@@ -150,22 +167,29 @@ def ensure_workspace(device, nbytes: int):
 
 def attention(q, k, v, *, causal=False, seqused_k=None, scale=None, out=None, lse=None,
               return_lse=True, variant=None):
-    """out, lse = softmax(scale * q k^T + mask) v for bf16 BSHD cuda tensors.
+    """out, lse = softmax(scale * q k^T + mask) v for bf16 or fp16 cuda tensors.
 
-    q [B, Sq, Hq, D]; k, v [B, Sk, Hkv, D]; seqused_k int32 [B] on the same
-    device or None.  ``scale`` defaults to 1/sqrt(D).  Returns (out, lse)
-    with lse [B, Hq, Sq] float32 (None when ``return_lse`` is False and no
-    ``lse`` tensor is passed).  ``variant`` = (qt, nw, kw, bn, nst, kps)
-    runs that kernel variant through fa_fwd_variant instead of fa_fwd's
-    choice.
+    q [B, Sq, Hq, D]; k, v [B, Sk, Hkv, D], all of one dtype (bfloat16 or
+    float16), each a (batch, seq, heads, head_dim) view whose head_dim is
+    contiguous (e.g. slices of one fused QKV tensor); seqused_k int32 [B] on
+    the same device or None.  ``scale`` defaults to 1/sqrt(D).  Returns
+    (out, lse) with out like q (allocated contiguous when not passed; a
+    passed ``out`` may be a strided view) and lse [B, Hq, Sq] float32 (None
+    when ``return_lse`` is False and no ``lse`` tensor is passed).
+    Contiguous bf16 tensors go through fa_fwd, everything else through
+    fa_fwd_strided.  ``variant`` = (qt, nw, kw, bn, nst, kps) runs that kernel
+    variant through fa_fwd_variant (contiguous bf16 only).
     """
     import torch
 
+    dtypes = {torch.bfloat16: FA_BF16, torch.float16: FA_FP16}
+    if not isinstance(q, torch.Tensor) or q.dtype not in dtypes:
+        raise TypeError("q must be a bfloat16 or float16 cuda tensor")
     for name, t in (("q", q), ("k", k), ("v", v)):
-        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or not t.is_cuda:
-            raise TypeError(f"{name} must be a bfloat16 cuda tensor")
-        if t.dim() != 4 or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous 4-D (batch, seq, heads, head_dim) tensor")
+        if not isinstance(t, torch.Tensor) or t.dtype != q.dtype or not t.is_cuda:
+            raise TypeError(f"{name} must be a cuda tensor of q's dtype ({q.dtype})")
+        if t.dim() != 4 or t.stride(3) != 1:
+            raise ValueError(f"{name} must be a 4-D (batch, seq, heads, head_dim) view with contiguous head_dim")
     B, Sq, Hq, D = q.shape
     Bk, Sk, Hkv, Dk = k.shape
     if tuple(v.shape) != tuple(k.shape) or Bk != B or Dk != D:
@@ -178,9 +202,9 @@ def attention(q, k, v, *, causal=False, seqused_k=None, scale=None, out=None, ls
                 or not seqused_k.is_contiguous():
             raise ValueError("seqused_k must be a contiguous int32 tensor of B entries on q's device")
     if out is None:
-        out = torch.empty_like(q)
-    elif out.shape != q.shape or out.dtype != torch.bfloat16 or out.device != dev or not out.is_contiguous():
-        raise ValueError("out must be a contiguous bf16 tensor shaped like q")
+        out = torch.empty((B, Sq, Hq, D), dtype=q.dtype, device=dev)
+    elif tuple(out.shape) != (B, Sq, Hq, D) or out.dtype != q.dtype or out.device != dev or out.stride(3) != 1:
+        raise ValueError("out must be a tensor shaped and typed like q with contiguous head_dim")
     if lse is None and return_lse:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev)
     elif lse is not None and (tuple(lse.shape) != (B, Hq, Sq) or lse.dtype != torch.float32
@@ -189,18 +213,26 @@ def attention(q, k, v, *, causal=False, seqused_k=None, scale=None, out=None, ls
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     causal = bool(causal)
+    dense = q.dtype == torch.bfloat16 and all(t.is_contiguous() for t in (q, k, v, out))
+    if variant is not None and not dense:
+        raise ValueError("variant is only available for contiguous bfloat16 tensors")
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), 0 if lse is None else lse.data_ptr())
     sq = 0 if seqused_k is None else seqused_k.data_ptr()
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
-        if variant is None:
+        if variant is not None:
+            ensure_workspace(dev, fa_fwd_variant_workspace_bytes(B, Sq, Sk, Hq, Hkv, D, causal, *variant))
+            rc = fa_fwd_variant(*ptrs, B, Sq, Sk, Hq, Hkv, D, causal, sq, float(scale), *variant, stream)
+            where = "fa_fwd_variant"
+        elif dense:
             ensure_workspace(dev, fa_fwd_workspace_bytes(B, Sq, Sk, Hq, Hkv, D, causal))
             rc = fa_fwd(*ptrs, B, Sq, Sk, Hq, Hkv, D, causal, sq, float(scale), stream)
             where = "fa_fwd"
         else:
-            ensure_workspace(dev, fa_fwd_variant_workspace_bytes(B, Sq, Sk, Hq, Hkv, D, causal, *variant))
-            rc = fa_fwd_variant(*ptrs, B, Sq, Sk, Hq, Hkv, D, causal, sq, float(scale), *variant, stream)
-            where = "fa_fwd_variant"
+            ensure_workspace(dev, fa_fwd_workspace_bytes(B, Sq, Sk, Hq, Hkv, D, causal))
+            rc = fa_fwd_strided(*ptrs, B, Sq, Sk, Hq, Hkv, D, q.stride()[:3], k.stride()[:3], v.stride()[:3],
+                                out.stride()[:3], dtypes[q.dtype], causal, sq, float(scale), stream)
+            where = "fa_fwd_strided"
     if rc != FA_OK:
         raise FAError(rc, where)
     return out, lse

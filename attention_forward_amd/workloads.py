@@ -77,8 +77,9 @@ WORKLOAD_ORDER = list(WORKLOADS)
 
 
 def make_custom(B, Sq, Sk, Hq, Hkv, D, *, seed, n_valid=None, pad_value=1.0e4,
-                q_scale=1.0, k_scale=1.0, v_scale=1.0):
-    """Seeded bf16 CPU tensors q [B,Sq,Hq,D], k and v [B,Sk,Hkv,D].
+                q_scale=1.0, k_scale=1.0, v_scale=1.0, dtype=torch.bfloat16):
+    """Seeded CPU tensors q [B,Sq,Hq,D], k and v [B,Sk,Hkv,D] of ``dtype``
+    (bfloat16 by default, or float16), drawn N(0,1) in fp32 and rounded.
 
     ``n_valid`` may be an int (same for all batch entries) or a sequence of
     B ints; rows ``[n_valid[b], Sk)`` of K and V are set to ``pad_value``
@@ -89,7 +90,7 @@ def make_custom(B, Sq, Sk, Hq, Hkv, D, *, seed, n_valid=None, pad_value=1.0e4,
     q = torch.randn(B, Sq, Hq, D, generator=g, dtype=torch.float32) * q_scale
     k = torch.randn(B, Sk, Hkv, D, generator=g, dtype=torch.float32) * k_scale
     v = torch.randn(B, Sk, Hkv, D, generator=g, dtype=torch.float32) * v_scale
-    q, k, v = (t.to(torch.bfloat16) for t in (q, k, v))
+    q, k, v = (t.to(dtype) for t in (q, k, v))
     seqused = None
     if n_valid is not None:
         lens = [int(n_valid)] * B if isinstance(n_valid, int) else [int(x) for x in n_valid]
@@ -103,9 +104,9 @@ def make_custom(B, Sq, Sk, Hq, Hkv, D, *, seed, n_valid=None, pad_value=1.0e4,
     return q, k, v, seqused
 
 
-def make_inputs(name_or_workload, *, seed=None, pad_value=1.0e4):
-    """Inputs for one named workload (CPU bf16 tensors, seqused_k or None)."""
+def make_inputs(name_or_workload, *, seed=None, pad_value=1.0e4, dtype=torch.bfloat16):
+    """Inputs for one named workload (CPU tensors, seqused_k or None)."""
     w = WORKLOADS[name_or_workload] if isinstance(name_or_workload, str) else name_or_workload
     return make_custom(w.B, w.Sq, w.Sk, w.Hq, w.Hkv, w.D,
                        seed=w.seed if seed is None else seed,
-                       n_valid=w.n_valid, pad_value=pad_value)
+                       n_valid=w.n_valid, pad_value=pad_value, dtype=dtype)

@@ -37,16 +37,19 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 1
+#define FA_ABI_VERSION 2
 
 /* Status codes. */
 enum {
   FA_OK = 0,
   FA_ERR_NULL = 1,        /* a required pointer is NULL */
   FA_ERR_SHAPE = 2,       /* a size is < 1, Hq % Hkv != 0, or a size overflows 32-bit indexing
-                             (element counts of q and k, or Sk*Hkv*D*2 bytes per batch entry, >= 2^31) */
-  FA_ERR_UNSUPPORTED = 3, /* D not in {64, 72, 256}; causal with Sq != Sk or with seqused_k; variant not compiled */
-  FA_ERR_ALIGN = 4,       /* q, k, v, out not 16-byte aligned; lse or seqused_k not 4-byte aligned */
+                             (element counts of q and k, or Sk*Hkv*D*2 bytes per batch entry, >= 2^31);
+                             fa_fwd_strided: also bad strides (see there) */
+  FA_ERR_UNSUPPORTED = 3, /* D not in {64, 72, 256}; causal with Sq != Sk or with seqused_k; variant not
+                             compiled; unknown element type */
+  FA_ERR_ALIGN = 4,       /* q, k, v, out not 16-byte aligned (or strides not multiples of 8 elements);
+                             lse or seqused_k not 4-byte aligned */
   FA_ERR_SCALE = 5,       /* scale not finite or not > 0 */
   FA_ERR_WORKSPACE = 6,   /* the split-KV path needs a workspace that is missing or too small */
   FA_ERR_LAUNCH = 7,      /* the HIP runtime rejected a kernel launch */
@@ -85,8 +88,52 @@ int fa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
            int B, int Sq, int Sk, int Hq, int Hkv, int D, int causal,
            const int32_t* seqused_k, float scale, hipStream_t stream);
 
+/* Element types of q, k, v and out (fa_fwd_strided). */
+enum {
+  FA_BF16 = 0,  /* bfloat16; out rounded to nearest even */
+  FA_FP16 = 1   /* IEEE half; out rounded to nearest even */
+};
+
+/* fa_fwd_strided: fa_fwd over strided views and either element type.
+ *
+ * The self-attention of the GROOT action head reads the fused QKV GEMM
+ * output in place (token stride 3*H*D), dropping the split copies
+ * ("GROOT N1.7 update: Thor NVFP4 + FA4 performance tier", section "What is
+ * in the tier"); fp16 is the other element type of the pages' attention
+ * kernels (the fp16 decoder attention of "pi05_thor_decoder_fp4_e2e.md",
+ * section "Fused GeGLU FFN in the Decoder"; the fp16 and bf16 FlashAttention-2
+ * forwards of "deployment_rtx4090.md").
+ *
+ *   q, out     (batch, position, head, head_dim) views: element (b, s, h, d)
+ *              at base + b*x_sb + s*x_ss + h*x_sh + d (strides in ELEMENTS;
+ *              head_dim is contiguous)
+ *   k, v       (batch, key, kv head, head_dim) views, same rule with their
+ *              own strides
+ *   dtype      FA_BF16 or FA_FP16, for q, k, v and out alike (fp32
+ *              accumulation, P rounded to the element type)
+ *   Everything else (lse [B, Hq, Sq] fp32 contiguous, seqused_k, causal,
+ *   scale, stream, workspace) is as for fa_fwd, and the kernel variant is
+ *   the one fa_fwd_plan reports.  With contiguous strides
+ *   (S*H*D, H*D, D) and FA_BF16 it computes exactly what fa_fwd does.
+ * Extra requirements: strides >= 0 and multiples of 8 elements (16-byte
+ * rows, FA_ERR_ALIGN otherwise); key rows of one head do not overlap
+ * (k_ss, v_ss >= D when Sk > 1) and no two output rows overlap
+ * (FA_ERR_SHAPE); Sk*k_ss*2 and Sk*v_ss*2 bytes, and the bytes from a
+ * batch entry's first query row to its last, below 2^31 (FA_ERR_SHAPE);
+ * out and lse must not share a byte with the span of q, k or v
+ * (FA_ERR_ALIAS).  q, k and v may share memory (e.g. one fused QKV buffer).
+ */
+int fa_fwd_strided(const void* q, const void* k, const void* v, void* out, float* lse,
+                   int B, int Sq, int Sk, int Hq, int Hkv, int D,
+                   int64_t q_sb, int64_t q_ss, int64_t q_sh,
+                   int64_t k_sb, int64_t k_ss, int64_t k_sh,
+                   int64_t v_sb, int64_t v_ss, int64_t v_sh,
+                   int64_t o_sb, int64_t o_ss, int64_t o_sh,
+                   int dtype, int causal, const int32_t* seqused_k, float scale, hipStream_t stream);
+
 /* Bytes of workspace fa_fwd needs for this shape (0: none).  Pure host
- * arithmetic; returns 0 for invalid shapes as well. */
+ * arithmetic; returns 0 for invalid shapes as well.  The same figure holds
+ * for fa_fwd_strided (the workspace does not depend on strides or dtype). */
 size_t fa_fwd_workspace_bytes(int B, int Sq, int Sk, int Hq, int Hkv, int D, int causal);
 
 /* Registers a caller-owned device buffer as the split-KV workspace of the

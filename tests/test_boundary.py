@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert fa.fa_abi_version() == 1
+    assert fa.fa_abi_version() == 2
     for code in range(9):
         assert fa.fa_status_string(code).startswith("FA_")
     assert "UNKNOWN" in fa.fa_status_string(99)
@@ -87,6 +87,53 @@ def _call(**over):
 ])
 def test_invalid_arguments_return_their_code(lib, over, code):
     assert _call(**over) == code
+
+
+def _call_strided(qs=None, ks=None, vs=None, os_=None, dtype=fa.FA_BF16, **over):
+    """fa_fwd_strided with contiguous strides unless overridden."""
+    a = dict(q=Q, k=K, v=V, out=O, lse=L, B=1, Sq=64, Sk=64, Hq=8, Hkv=1, D=256, causal=0,
+             seqused_k=0, scale=0.0625, stream=0)
+    a.update(over)
+    B, Sq, Sk, Hq, Hkv, D = (a[x] for x in ("B", "Sq", "Sk", "Hq", "Hkv", "D"))
+    qs = qs or (Sq * Hq * D, Hq * D, D)
+    ks = ks or (Sk * Hkv * D, Hkv * D, D)
+    vs = vs or ks
+    os_ = os_ or (Sq * Hq * D, Hq * D, D)
+    return fa.fa_fwd_strided(a["q"], a["k"], a["v"], a["out"], a["lse"], B, Sq, Sk, Hq, Hkv, D,
+                             qs, ks, vs, os_, dtype, a["causal"], a["seqused_k"], a["scale"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=0), fa.FA_ERR_NULL),
+    (dict(B=0), fa.FA_ERR_SHAPE),
+    (dict(Hq=6, Hkv=4), fa.FA_ERR_SHAPE),
+    (dict(D=128), fa.FA_ERR_UNSUPPORTED),
+    (dict(causal=1, seqused_k=S), fa.FA_ERR_UNSUPPORTED),
+    (dict(scale=0.0), fa.FA_ERR_SCALE),
+    (dict(q=Q + 8), fa.FA_ERR_ALIGN),
+    (dict(out=Q), fa.FA_ERR_ALIAS),
+    (dict(lse=K + 64), fa.FA_ERR_ALIAS),
+    # element type
+    (dict(dtype=2), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=-1), fa.FA_ERR_UNSUPPORTED),
+    # strides: multiples of 8 elements (16-byte rows)
+    (dict(qs=(64 * 8 * 256, 8 * 256 + 4, 256)), fa.FA_ERR_ALIGN),
+    (dict(ks=(64 * 256, 260, 256)), fa.FA_ERR_ALIGN),
+    (dict(os_=(64 * 8 * 264, 8 * 264, 260)), fa.FA_ERR_ALIGN),
+    # negative strides, overlapping key rows, overlapping output rows
+    (dict(qs=(-8, 8 * 256, 256)), fa.FA_ERR_SHAPE),
+    (dict(ks=(64 * 256, 128, 256)), fa.FA_ERR_SHAPE),
+    (dict(vs=(64 * 256, 0, 256)), fa.FA_ERR_SHAPE),
+    (dict(os_=(64 * 8 * 256, 0, 256)), fa.FA_ERR_SHAPE),
+    (dict(os_=(64 * 8 * 256, 8 * 256, 128)), fa.FA_ERR_SHAPE),
+    # 32-bit key offsets of one (batch, kv head)
+    (dict(ks=(0, 1 << 24, 256)), fa.FA_ERR_SHAPE),
+    # out inside the span of a strided q (one buffer)
+    (dict(out=Q + 512, os_=(64 * 8 * 3 * 256, 8 * 3 * 256, 256), qs=(64 * 8 * 3 * 256, 8 * 3 * 256, 256)),
+     fa.FA_ERR_ALIAS),
+])
+def test_strided_invalid_arguments_return_their_code(lib, over, code):
+    assert _call_strided(**over) == code
 
 
 def test_check_order_is_null_then_shape(lib):
