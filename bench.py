@@ -48,8 +48,8 @@ def algorithmic(w):
     """Algorithmic FLOPs and HBM bytes of one call: 4*D per attended
     (query, key) pair; bytes = Q + valid K + valid V + out (bf16) + lse (fp32)."""
     n = w.valid_keys
-    if w.causal:
-        pairs = w.B * w.Hq * sum(min(i + 1, n) for i in range(w.Sq))
+    if w.causal:  # query i attends keys 0 .. i + n - Sq (the last query lines up with the last key)
+        pairs = w.B * w.Hq * sum(max(0, min(i + 1 + n - w.Sq, n)) for i in range(w.Sq))
     else:
         pairs = w.B * w.Hq * w.Sq * n
     flops = 4 * w.D * pairs

@@ -36,7 +36,13 @@ Readings taken where the pages are silent:
 * The Q head h reads K/V head floor(h / (Hq / Hkv)).
 * seqused_k[b] is clamped to [0, Sk]; an empty key set gives out = 0 and
   lse = -inf.
-* Causal means key j is attended by query i iff j <= i, with Sq == Sk.
+* Causal means key j is attended by query i iff j <= i + (n_b - Sq): the
+  last query row lines up with the last valid key (the bottom-right
+  alignment of FlashAttention, whose input contract the model card's
+  runtime follows).  With Sq == Sk and no seqused_k this is j <= i, the
+  causal prefill of the PI0.5 demo; with fewer queries than keys it is a
+  chunk of new positions attending a cache, and with more queries than keys
+  the first Sq - n_b rows attend nothing.
 * sigma is float64(float32(scale)): the value the device receives.
 """
 
@@ -84,9 +90,9 @@ def attended_pairs(batch, sq, sk, hq, causal, seqused_k) -> int:
     total = 0
     for b in range(batch):
         if causal:
-            # query i attends keys 0..min(i, n_b - 1)
+            # query i attends keys 0..min(i + n_b - Sq, n_b - 1)
             i = np.arange(sq, dtype=np.int64)
-            total += int(np.minimum(i + 1, n[b]).clip(min=0).sum())
+            total += int(np.minimum(i + 1 + (n[b] - sq), n[b]).clip(min=0).sum())
         else:
             total += sq * int(n[b])
     return total * hq
@@ -98,7 +104,8 @@ def attention_ref(q, k, v, *, causal=False, seqused_k=None, scale=None):
     Args:
       q: array [B, Sq, Hq, D] (any float dtype; widened exactly to float64).
       k, v: arrays [B, Sk, Hkv, D]; Hq must be a multiple of Hkv.
-      causal: key j is attended by query i only when j <= i (needs Sq == Sk).
+      causal: key j is attended by query i only when j <= i + (n_b - Sq),
+        n_b the number of valid keys of batch entry b.
       seqused_k: None, or B integers: keys j >= seqused_k[b] are not read.
       scale: softmax temperature; None means 1/sqrt(D).
 
@@ -116,8 +123,6 @@ def attention_ref(q, k, v, *, causal=False, seqused_k=None, scale=None):
         raise ValueError("k and v must be [B, Sk, Hkv, D] matching q")
     if Hkv < 1 or Hq % Hkv != 0:
         raise ValueError("Hq must be a multiple of Hkv")
-    if causal and Sq != Sk:
-        raise ValueError("causal attention is defined here for Sq == Sk only")
     sigma = effective_scale(scale, D)
     group = Hq // Hkv
     n = valid_lengths(B, Sk, seqused_k)
@@ -132,16 +137,17 @@ def attention_ref(q, k, v, *, causal=False, seqused_k=None, scale=None):
         # Padding rows j >= n_b are never read: slice them off first.
         kb = k[b, :nb]  # [nb, Hkv, D]
         vb = v[b, :nb]
+        i = np.arange(Sq)[:, None]
+        j = np.arange(nb)[None, :]
+        keep = (j <= i + (nb - Sq)) if causal else np.ones((Sq, nb), dtype=bool)
+        rows = np.any(keep, axis=1)  # queries that attend at least one key
         for h in range(Hq):
             hk = h // group
             s = sigma * np.matmul(q[b, :, h, :], kb[:, hk, :].T)  # [Sq, nb]
-            if causal:
-                i = np.arange(Sq)[:, None]
-                j = np.arange(nb)[None, :]
-                s = np.where(j <= i, s, -np.inf)
-            m = np.max(s, axis=1, keepdims=True)  # finite: key 0 is always attended
+            s = np.where(keep, s, -np.inf)[rows]
+            m = np.max(s, axis=1, keepdims=True)  # finite: every kept row attends a key
             w = np.exp(s - m)
             l = np.sum(w, axis=1, keepdims=True)
-            out[b, :, h, :] = np.matmul(w, vb[:, hk, :]) / l
-            lse[b, h, :] = (m + np.log(l))[:, 0]
+            out[b, rows, h, :] = np.matmul(w, vb[:, hk, :]) / l
+            lse[b, h, rows] = (m + np.log(l))[:, 0]
     return out, lse

@@ -8,7 +8,8 @@ AssertionError when the implementation disagrees with:
 * a pure-Python brute force in 50-digit mpmath on tiny inputs,
 * invariants the definition implies (padding is never read, key
   permutation, shift of all keys, linearity in V, GQA equals MHA with
-  replicated K/V, causal row i equals non-causal attention over keys 0..i),
+  replicated K/V, causal row i equals non-causal attention over keys
+  0..i + n_b - Sq),
 * numerical stability at logits of size 1e4 (against mpmath).
 
 The same pins run against the oracle and against mutants of it with a
@@ -53,7 +54,8 @@ def brute_force(q, k, v, *, causal=False, seqused_k=None, scale=None):
         for h in range(Hq):
             hk = h // g
             for i in range(Sq):
-                keys = [j for j in range(nb) if (not causal or j <= i)]
+                # causal: the last query lines up with the last valid key
+                keys = [j for j in range(nb) if (not causal or j - i <= nb - Sq)]
                 if not keys:
                     lse[b, h, i] = -math.inf
                     continue
@@ -168,6 +170,9 @@ def pin_brute_force(impl, cases=None):
             dict(B=2, Sq=4, Sk=4, Hq=4, Hkv=2, D=5, causal=True, seq=None),
             dict(B=2, Sq=3, Sk=6, Hq=2, Hkv=1, D=4, causal=False, seq=[6, 2]),
             dict(B=1, Sq=5, Sk=5, Hq=3, Hkv=3, D=2, causal=True, seq=None),
+            dict(B=1, Sq=2, Sk=5, Hq=2, Hkv=1, D=3, causal=True, seq=None),
+            dict(B=2, Sq=4, Sk=6, Hq=2, Hkv=2, D=2, causal=True, seq=[5, 2]),
+            dict(B=1, Sq=5, Sk=3, Hq=1, Hkv=1, D=3, causal=True, seq=None),
         ]
     for c in cases:
         q = _randn(rng, c["B"], c["Sq"], c["Hq"], c["D"])
@@ -281,6 +286,34 @@ def pin_causal_prefix(impl):
         _close(lse[:, :, i:i + 1], li, 1e-13, what=f"causal row {i} lse")
 
 
+def pin_causal_bottom_right(impl):
+    """Causal with Sq != n_b (n_b valid keys): query i attends keys
+    0..i + n_b - Sq.  Row i equals non-causal attention over that key
+    prefix; a single query (decode) attends every valid key; with more
+    queries than keys the first Sq - n_b rows attend nothing (out 0,
+    lse -inf); padding past seqused_k is never read."""
+    rng = _rng(24)
+    D = 4
+    for Sq, Sk, seq in ((3, 7, None), (1, 6, None), (6, 4, None), (4, 9, [6]), (5, 9, [3])):
+        q = _randn(rng, 1, Sq, 2, D)
+        k = _randn(rng, 1, Sk, 1, D)
+        v = _randn(rng, 1, Sk, 1, D)
+        n = Sk if seq is None else seq[0]
+        if seq is not None:
+            k[0, n:] = np.nan
+            v[0, n:] = np.nan
+        sq = None if seq is None else np.array(seq)
+        out, lse = impl(q, k, v, causal=True, seqused_k=sq)
+        for i in range(Sq):
+            last = i + n - Sq  # last attended key
+            if last < 0:
+                assert np.all(out[0, i] == 0.0) and np.all(np.isneginf(lse[0, :, i])), f"empty row {i}"
+                continue
+            oi, li = impl(q[:, i:i + 1], k[:, :last + 1], v[:, :last + 1])
+            _close(out[:, i:i + 1], oi, 1e-13, what=f"bottom-right row {i} out ({Sq},{Sk},{seq})")
+            _close(lse[:, :, i:i + 1], li, 1e-13, what=f"bottom-right row {i} lse ({Sq},{Sk},{seq})")
+
+
 def pin_scale(impl):
     """The logits are sigma * q.k with sigma = float32(scale); the default
     scale is 1/sqrt(D)."""
@@ -325,6 +358,7 @@ ALL_PINS = [
     pin_v_linearity,
     pin_gqa_is_replicated_mha,
     pin_causal_prefix,
+    pin_causal_bottom_right,
     pin_scale,
     pin_large_logits,
 ]

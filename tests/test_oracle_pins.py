@@ -34,9 +34,6 @@ def test_oracle_pin(pin):
     use_seq=st.booleans(),
 )
 def test_oracle_matches_brute_force_random_shapes(B, Sq, Sk, Hkv, g, D, causal, seq_frac, use_seq):
-    if causal:
-        Sk = Sq
-        use_seq = False
     seq = None
     if use_seq:
         seq = np.array([int(round(f * Sk)) for f in seq_frac[:B]])
@@ -49,18 +46,21 @@ def test_oracle_matches_brute_force_random_shapes(B, Sq, Sk, Hkv, g, D, causal, 
 MUTATIONS = [
     ("GQA head index h % Hkv", "hk = h // group", "hk = h % Hkv"),
     ("no max subtraction", "m = np.max(s, axis=1, keepdims=True)", "m = np.zeros_like(s[:, :1])"),
-    ("lse drops the max term", "lse[b, h, :] = (m + np.log(l))[:, 0]", "lse[b, h, :] = np.log(l)[:, 0]"),
-    ("lse in log2", "lse[b, h, :] = (m + np.log(l))[:, 0]", "lse[b, h, :] = (m + np.log2(l))[:, 0]"),
+    ("lse drops the max term", "lse[b, h, rows] = (m + np.log(l))[:, 0]", "lse[b, h, rows] = np.log(l)[:, 0]"),
+    ("lse in log2", "lse[b, h, rows] = (m + np.log(l))[:, 0]", "lse[b, h, rows] = (m + np.log2(l))[:, 0]"),
     ("scale dropped", "s = sigma * np.matmul", "s = np.matmul"),
     ("scale divides", "s = sigma * np.matmul(q[b, :, h, :], kb[:, hk, :].T)",
      "s = np.matmul(q[b, :, h, :], kb[:, hk, :].T) / sigma"),
-    ("causal j < i", "s = np.where(j <= i, s, -np.inf)", "s = np.where(j < i, s, -np.inf)"),
-    ("causal mask transposed", "s = np.where(j <= i, s, -np.inf)", "s = np.where(j >= i, s, -np.inf)"),
+    ("causal j < i", "keep = (j <= i + (nb - Sq))", "keep = (j < i + (nb - Sq))"),
+    ("causal mask transposed", "keep = (j <= i + (nb - Sq))", "keep = (j >= i + (nb - Sq))"),
+    ("causal aligned top-left", "keep = (j <= i + (nb - Sq))", "keep = (j <= i)"),
+    ("causal offset from the buffer length", "keep = (j <= i + (nb - Sq))", "keep = (j <= i + (Sk - Sq))"),
+    ("rows without keys computed", "rows = np.any(keep, axis=1)", "rows = np.ones(Sq, dtype=bool)"),
     ("padding read", "kb = k[b, :nb]", "kb = k[b, :]"),
-    ("V replaced by K", "out[b, :, h, :] = np.matmul(w, vb[:, hk, :]) / l",
-     "out[b, :, h, :] = np.matmul(w, kb[:, hk, :]) / l"),
-    ("no normalisation", "out[b, :, h, :] = np.matmul(w, vb[:, hk, :]) / l",
-     "out[b, :, h, :] = np.matmul(w, vb[:, hk, :])"),
+    ("V replaced by K", "out[b, rows, h, :] = np.matmul(w, vb[:, hk, :]) / l",
+     "out[b, rows, h, :] = np.matmul(w, kb[:, hk, :]) / l"),
+    ("no normalisation", "out[b, rows, h, :] = np.matmul(w, vb[:, hk, :]) / l",
+     "out[b, rows, h, :] = np.matmul(w, vb[:, hk, :])"),
     ("exp sign flipped", "w = np.exp(s - m)", "w = np.exp(m - s)"),
     ("exp base 2", "w = np.exp(s - m)", "w = np.exp2(s - m)"),
     ("empty row lse 0", "lse = np.full((B, Hq, Sq), -np.inf, dtype=np.float64)",
@@ -104,3 +104,7 @@ def test_attended_pairs_counts():
     assert ref.attended_pairs(3, 256, 256, 16, False, None) == 3 * 16 * 256 * 256
     assert ref.attended_pairs(1, 41, 1056, 8, False, [1009]) == 8 * 41 * 1009
     assert ref.attended_pairs(2, 4, 6, 1, False, [0, 9]) == 4 * 6
+    # causal, bottom-right: query i attends min(i + 1 + n - Sq, n) keys (>= 0)
+    assert ref.attended_pairs(1, 41, 1056, 8, True, [1009]) == 8 * sum(969 + i for i in range(41))
+    assert ref.attended_pairs(1, 1, 10, 2, True, None) == 2 * 10
+    assert ref.attended_pairs(1, 6, 4, 1, True, None) == 0 + 0 + 1 + 2 + 3 + 4
