@@ -69,8 +69,10 @@ void finish_plan(Plan& pl, int B, int Sq, int Sk, int Hq, int Hkv, int causal) {
   pl.ws_o_bytes = pl.ws_ml_bytes = pl.ws_bytes = 0;
   if (!pl.launch.split) return;
   if (causal) {
-    const long long kmax_last = (std::min((long long)pl.nrb * rows, (long long)pl.Mp) - 1) / g + 1;
-    pl.zmax = (int)cdiv(kmax_last, pl.kps);
+    // keys of the last row block (the last query attends the whole buffer)
+    const long long last = (std::min((long long)pl.nrb * rows, (long long)pl.Mp) - 1) / g + (Sk - Sq) + 1;
+    const long long kmax_last = std::max(0ll, std::min((long long)Sk, last));
+    pl.zmax = (int)std::max(1ll, cdiv(kmax_last, pl.kps));
   } else {
     pl.launch.nsplit = (int)cdiv(Sk, pl.kps);
     pl.zmax = pl.launch.nsplit;
@@ -87,8 +89,8 @@ void finish_plan(Plan& pl, int B, int Sq, int Sk, int Hq, int Hkv, int causal) {
 //  * Head dim 256: key-split workgroups (32 rows, four waves over the keys),
 //    which read half the LDS bytes per MFMA of the row-split kernel.
 //  * Smaller head dims: row-split workgroups, one wave per 16 packed rows.
-// When the single-pass grid is at most half the compute units (non-causal),
-// the key range is split into fixed-size ranges, merged afterwards by the
+// When the single-pass grid is at most half the compute units, the key
+// range is split into fixed-size ranges, merged afterwards by the
 // combine kernel.  The range size depends on the grid size only, not on the
 // key buffer length, so a padded buffer and the same keys without the
 // padding are split at the same boundaries (the extra ranges of the padded
@@ -114,7 +116,7 @@ Plan default_plan(int B, int Sq, int Sk, int Hq, int Hkv, int D, int causal) {
   const int rows = rows_per_block(pl.launch);
   const long long base = cdiv(Mp, rows) * BH;
   pl.kps = 0;
-  if (!causal && base <= kTargetWorkgroups / 2) {
+  if (base <= kTargetWorkgroups / 2) {
     const int kps = base <= 32 ? 128 : (base <= 64 ? 256 : 512);
     if (Sk > kps) pl.kps = kps;
   }
@@ -148,7 +150,6 @@ int check_args(const void* q, const void* k, const void* v, void* out, float* ls
   if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return FA_ERR_NULL;
   int rc = check_shape(B, Sq, Sk, Hq, Hkv, D, causal);
   if (rc != FA_OK) return rc;
-  if (causal && (Sq != Sk || seqused_k != nullptr)) return FA_ERR_UNSUPPORTED;
   if (!(scale > 0.0f) || !isfinite(scale)) return FA_ERR_SCALE;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return FA_ERR_ALIGN;
   if ((lse != nullptr && !aligned(lse, 4)) || (seqused_k != nullptr && !aligned(seqused_k, 4)))
@@ -206,7 +207,6 @@ int check_strided(const void* q, const void* k, const void* v, void* out, float*
   if (((long long)(Sq - 1) * vq.ss + (long long)(Hq - 1) * vq.sh + D) * 2 >= (1ll << 31)) return FA_ERR_SHAPE;
   if (!supported_d(D)) return FA_ERR_UNSUPPORTED;
   if (dtype != fa::kBf16 && dtype != fa::kF16) return FA_ERR_UNSUPPORTED;
-  if (causal && (Sq != Sk || seqused_k != nullptr)) return FA_ERR_UNSUPPORTED;
   if (!(scale > 0.0f) || !isfinite(scale)) return FA_ERR_SCALE;
   // Key rows of one head may not overlap (a row ends before the next starts),
   // and every output row is written once.
@@ -267,6 +267,7 @@ int run(const Plan& pl, const void* q, const void* k, const void* v, void* out, 
   p.Hkv = Hkv;
   p.g = Hq / Hkv;
   p.Mp = pl.Mp;
+  p.coff = Sk - Sq;
   p.kps = pl.kps;
   p.nrb = pl.nrb;
   p.zmax = pl.zmax;
@@ -305,7 +306,7 @@ const char* fa_status_string(int code) {
     case FA_OK: return "FA_OK: success";
     case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
     case FA_ERR_SHAPE: return "FA_ERR_SHAPE: invalid sizes or strides (need all sizes >= 1, Hq % Hkv == 0, offsets within 32 bits, non-negative strides, key rows and output rows that do not overlap)";
-    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: unsupported head_dim (64, 72, 256), element type, kernel variant, or causal with Sq != Sk or with seqused_k";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: unsupported head_dim (64, 72, 256), element type, or kernel variant";
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: q/k/v/out must be 16-byte aligned with strides in multiples of 8 elements, lse/seqused_k 4-byte aligned";
     case FA_ERR_SCALE: return "FA_ERR_SCALE: scale must be finite and > 0";
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: split-KV path needs a registered workspace of fa_fwd_workspace_bytes() bytes";

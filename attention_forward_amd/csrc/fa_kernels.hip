@@ -291,9 +291,13 @@ __device__ __forceinline__ void softmax_tile(f32x4_t (&sacc)[G::MT][QT], uint32_
       for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[mt][t][r]);
     mx = group_max(mx) * c2;
     const float m_new = fmaxf(m_run[t], mx);
-    if (__ballot(m_new > m_run[t] + kRescaleThreshold) != 0) {
-      const float alpha = __builtin_amdgcn_exp2f(m_run[t] - m_new);  // 0 when m_run = -inf
-      m_run[t] = m_new;
+    // The branch is taken when any row of the wave moves; each row then
+    // rescales by its own factor (1 for a row whose max stayed, including a
+    // row that has attended no key yet, whose max is still -inf).
+    const bool moved = m_new > m_run[t] + kRescaleThreshold;
+    if (__ballot(moved) != 0) {
+      const float alpha = moved ? __builtin_amdgcn_exp2f(m_run[t] - m_new) : 1.f;  // 0 when m_run = -inf
+      m_run[t] = moved ? m_new : m_run[t];
       l_run[t] *= alpha;
 #pragma unroll
       for (int i = 0; i < G::DT; ++i) oacc[i][t] *= alpha;
@@ -489,6 +493,17 @@ __device__ __forceinline__ void pipe_tile(f32x4_t (&s_nxt)[G::MT][QT], f32x4_t (
   mfmas(C2, G::KC);
 }
 
+// Causal: keys a row block may attend, as planned on the host for the full
+// key buffer -- up to the diagonal key of the block's last row, with the
+// last query aligned to the last key (offset coff = Sk - Sq) -- clamped to
+// [0, Sk].  Grids and split counts come from this bound; inside a block the
+// range is narrowed to the valid keys (offset seqused_k - Sq).
+__host__ __device__ __forceinline__ int causal_kmax(int rb, int rows, int Mp, int g, int coff, int Sk) {
+  const int last_row = ((rb + 1) * rows < Mp ? (rb + 1) * rows : Mp) - 1;
+  const int k = last_row / g + coff + 1;
+  return k < 0 ? 0 : (k > Sk ? Sk : k);
+}
+
 struct RowBlock {
   int rb;      // row block index
   int z;       // key chunk (split) index
@@ -528,17 +543,18 @@ fwd_kernel(const FwdParams p) {
     const int nrb = (p.Mp + G::ROWS_WG - 1) / G::ROWS_WG;
     int item = blockIdx.x, rb = nrb - 1;
     for (; rb >= 0; --rb) {
-      const int kmax = (min((rb + 1) * G::ROWS_WG, p.Mp) - 1) / g + 1;
+      const int kmax = causal_kmax(rb, G::ROWS_WG, p.Mp, g, p.coff, p.Sk);
       const int nz = SPLIT ? (kmax + p.kps - 1) / p.kps : 1;
       if (item < nz) break;
       item -= nz;
     }
     blk.rb = rb;
     blk.z = item;
-    const int kmax = (min((rb + 1) * G::ROWS_WG, p.Mp) - 1) / g + 1;
+    const int kmax = causal_kmax(rb, G::ROWS_WG, p.Mp, g, p.coff, p.Sk);
     blk.kbeg = SPLIT ? item * p.kps : 0;
     blk.kend = SPLIT ? min(blk.kbeg + p.kps, kmax) : kmax;
-    blk.kend = min(blk.kend, nvalid);
+    // the valid keys, up to the diagonal of the block's last row
+    blk.kend = min(min(blk.kend, nvalid), (min((rb + 1) * G::ROWS_WG, p.Mp) - 1) / g + (nvalid - p.Sq) + 1);
   } else {
     blk.rb = rb_x;
     blk.z = SPLIT ? blockIdx.z : 0;
@@ -552,8 +568,11 @@ fwd_kernel(const FwdParams p) {
   typename G::E::v8 qf[QT][G::KC];
   int srow[QT];
   const bool wave_active = rw0 < p.Mp;
-  const int s_lo = min(rw0, p.Mp - 1) / g;
-  const int s_hi = (min(rw0 + 16 * QT, p.Mp) - 1) / g;
+  // Causal: diagonal keys (last attended key) of the wave's first and last
+  // rows; the last query lines up with the last valid key.
+  const int doff = CAUSAL ? nvalid - p.Sq : 0;
+  const int s_lo = min(rw0, p.Mp - 1) / g + doff;
+  const int s_hi = (min(rw0 + 16 * QT, p.Mp) - 1) / g + doff;
 
   f32x4_t oacc[G::DT][QT];
 #pragma unroll
@@ -647,7 +666,7 @@ fwd_kernel(const FwdParams p) {
     const bool ok = r < p.Mp;
     const int s = ok ? r / g : 0;
     const int hh = ok ? r - s * g : 0;
-    srow[t] = ok ? s : -1;
+    srow[t] = ok ? s + doff : -1;  // causal: the row's diagonal key
     const uint16_t* qp = p.q + b * p.q_sb + s * p.q_ss + (hk * g + hh) * p.q_sh;
 #pragma unroll
     for (int c = 0; c < G::KC; ++c) {
@@ -817,17 +836,18 @@ fwd_ks_kernel(const FwdParams p) {
     const int nrb = (p.Mp + ROWS - 1) / ROWS;
     int item = blockIdx.x, rb = nrb - 1;
     for (; rb >= 0; --rb) {
-      const int kmax = (min((rb + 1) * ROWS, p.Mp) - 1) / g + 1;
+      const int kmax = causal_kmax(rb, ROWS, p.Mp, g, p.coff, p.Sk);
       const int nz = SPLIT ? (kmax + p.kps - 1) / p.kps : 1;
       if (item < nz) break;
       item -= nz;
     }
     blk.rb = rb;
     blk.z = item;
-    const int kmax = (min((rb + 1) * ROWS, p.Mp) - 1) / g + 1;
+    const int kmax = causal_kmax(rb, ROWS, p.Mp, g, p.coff, p.Sk);
     blk.kbeg = SPLIT ? item * p.kps : 0;
     blk.kend = SPLIT ? min(blk.kbeg + p.kps, kmax) : kmax;
-    blk.kend = min(blk.kend, nvalid);
+    // the valid keys, up to the diagonal of the block's last row
+    blk.kend = min(min(blk.kend, nvalid), (min((rb + 1) * ROWS, p.Mp) - 1) / g + (nvalid - p.Sq) + 1);
   } else {
     blk.rb = blockIdx.x;
     blk.z = SPLIT ? blockIdx.z : 0;
@@ -836,7 +856,8 @@ fwd_ks_kernel(const FwdParams p) {
   }
   const int row0 = blk.rb * ROWS;
   const int kbeg = blk.kbeg, kend = blk.kend;
-  const int s_lo = min(row0, p.Mp - 1) / g;
+  const int doff = CAUSAL ? nvalid - p.Sq : 0;  // causal: diagonal key offset (last query <-> last valid key)
+  const int s_lo = min(row0, p.Mp - 1) / g + doff;
 
   typename G::E::v8 qf[QT][G::KC];
   int srow[QT];
@@ -933,7 +954,7 @@ fwd_ks_kernel(const FwdParams p) {
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
     const int r = row0 + 16 * t + col;
-    srow[t] = r < p.Mp ? r / g : -1;
+    srow[t] = r < p.Mp ? r / g + doff : -1;  // causal: the row's diagonal key
 #pragma unroll
     for (int c = 0; c < G::KC; ++c) {
       qf[t][c] = G::E::cast(*reinterpret_cast<const u32x4_t*>(smem + Q_OFF + (16 * t + col) * G::KSTR + c * 64 + grp * 16));
@@ -1067,8 +1088,7 @@ combine_kernel(const FwdParams p) {
   const int b = bh / p.Hkv, hk = bh - b * p.Hkv;
   int nz = p.zmax;
   if constexpr (CAUSAL) {
-    const int kmax = (min((rb + 1) * ROWS_WG, p.Mp) - 1) / g + 1;
-    nz = (kmax + p.kps - 1) / p.kps;
+    nz = (causal_kmax(rb, ROWS_WG, p.Mp, g, p.coff, p.Sk) + p.kps - 1) / p.kps;
   }
   const size_t slot_base = ((size_t)bh * p.nrb + rb) * p.zmax;
   float M = -INFINITY, L = 0.f;
@@ -1121,8 +1141,7 @@ static hipError_t launch_variant(const FwdParams& p, const LaunchPlan& plan, hip
   if (CAUSAL) {
     int items = 0;
     for (int rb = 0; rb < nrb; ++rb) {
-      const int kmax = (std::min((rb + 1) * G::ROWS_WG, p.Mp) - 1) / p.g + 1;
-      items += SPLIT ? (kmax + p.kps - 1) / p.kps : 1;
+      items += SPLIT ? (causal_kmax(rb, G::ROWS_WG, p.Mp, p.g, p.coff, p.Sk) + p.kps - 1) / p.kps : 1;
     }
     grid = dim3(items, p.B * p.Hkv, 1);
   } else {
@@ -1145,8 +1164,7 @@ static hipError_t launch_ks_variant(const FwdParams& p, const LaunchPlan& plan, 
   if (CAUSAL) {
     int items = 0;
     for (int rb = 0; rb < nrb; ++rb) {
-      const int kmax = (std::min((rb + 1) * ROWS, p.Mp) - 1) / p.g + 1;
-      items += SPLIT ? (kmax + p.kps - 1) / p.kps : 1;
+      items += SPLIT ? (causal_kmax(rb, ROWS, p.Mp, p.g, p.coff, p.Sk) + p.kps - 1) / p.kps : 1;
     }
     grid = dim3(items, p.B * p.Hkv, 1);
   } else {

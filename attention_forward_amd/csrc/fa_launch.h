@@ -22,6 +22,7 @@ struct FwdParams {
   int B, Sq, Sk, Hq, Hkv;
   int g;                   // Hq / Hkv
   int Mp;                  // packed rows per (batch, kv head) = Sq * g
+  int coff;                // Sk - Sq: causal diagonal offset of the full key buffer (grid planning)
   int kps;                 // keys per split (multiple of the key tile), split variants only
   int nrb;                 // row blocks per (batch, kv head)
   int zmax;                // most splits of any row block

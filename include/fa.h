@@ -46,8 +46,7 @@ enum {
   FA_ERR_SHAPE = 2,       /* a size is < 1, Hq % Hkv != 0, or a size overflows 32-bit indexing
                              (element counts of q and k, or Sk*Hkv*D*2 bytes per batch entry, >= 2^31);
                              fa_fwd_strided: also bad strides (see there) */
-  FA_ERR_UNSUPPORTED = 3, /* D not in {64, 72, 256}; causal with Sq != Sk or with seqused_k; variant not
-                             compiled; unknown element type */
+  FA_ERR_UNSUPPORTED = 3, /* D not in {64, 72, 256}; variant not compiled; unknown element type */
   FA_ERR_ALIGN = 4,       /* q, k, v, out not 16-byte aligned (or strides not multiples of 8 elements);
                              lse or seqused_k not 4-byte aligned */
   FA_ERR_SCALE = 5,       /* scale not finite or not > 0 */
@@ -67,8 +66,15 @@ enum {
  *              j >= seqused_k[b] of batch b are neither read nor attended.
  *              Values are clamped to [0, Sk] on the device.  A row with no
  *              attended key gets out = 0 and lse = -inf.
- *   causal     0 or 1.  With 1, query i attends key j only when j <= i; this
- *              requires Sq == Sk and seqused_k == NULL.
+ *   causal     0 or 1.  With 1, query i attends key j only when
+ *              j <= i + (n_b - Sq), n_b the valid keys of batch entry b
+ *              (Sk, or seqused_k[b]): the last query row lines up with the
+ *              last valid key, so Sq == Sk without seqused_k is the usual
+ *              j <= i prefill mask (the causal prefill of "Model Demo: PI0.5
+ *              End-to-End VLA Inference", section "Model stages"), and fewer
+ *              queries than keys is a chunk of new positions attending a
+ *              cache (decode: Sq = 1 attends every valid key).  Rows with
+ *              i + n_b - Sq < 0 attend nothing (out = 0, lse = -inf).
  *   scale      softmax temperature applied to q.k (finite, > 0), passed as
  *              float; use 1/sqrt(D) for the usual scaling.
  *   Hq % Hkv == 0; query head h reads K/V head h / (Hq / Hkv).

@@ -70,8 +70,6 @@ def _call(**over):
     (dict(B=1, Sq=1 << 20, Sk=64, Hq=8, Hkv=1, D=256), fa.FA_ERR_SHAPE),
     (dict(D=128), fa.FA_ERR_UNSUPPORTED),
     (dict(D=80), fa.FA_ERR_UNSUPPORTED),
-    (dict(causal=1, Sq=64, Sk=128), fa.FA_ERR_UNSUPPORTED),
-    (dict(causal=1, seqused_k=S), fa.FA_ERR_UNSUPPORTED),
     (dict(scale=0.0), fa.FA_ERR_SCALE),
     (dict(scale=-1.0), fa.FA_ERR_SCALE),
     (dict(scale=float("inf")), fa.FA_ERR_SCALE),
@@ -108,7 +106,6 @@ def _call_strided(qs=None, ks=None, vs=None, os_=None, dtype=fa.FA_BF16, **over)
     (dict(B=0), fa.FA_ERR_SHAPE),
     (dict(Hq=6, Hkv=4), fa.FA_ERR_SHAPE),
     (dict(D=128), fa.FA_ERR_UNSUPPORTED),
-    (dict(causal=1, seqused_k=S), fa.FA_ERR_UNSUPPORTED),
     (dict(scale=0.0), fa.FA_ERR_SCALE),
     (dict(q=Q + 8), fa.FA_ERR_ALIGN),
     (dict(out=Q), fa.FA_ERR_ALIAS),
