@@ -52,7 +52,8 @@ import math
 
 import numpy as np
 
-__all__ = ["attention_ref", "effective_scale", "valid_lengths", "attended_pairs"]
+__all__ = ["attention_ref", "attention_varlen_ref", "varlen_spans", "effective_scale", "valid_lengths",
+           "attended_pairs"]
 
 
 def effective_scale(scale, head_dim: int) -> float:
@@ -150,4 +151,65 @@ def attention_ref(q, k, v, *, causal=False, seqused_k=None, scale=None):
             l = np.sum(w, axis=1, keepdims=True)
             out[b, rows, h, :] = np.matmul(w, vb[:, hk, :]) / l
             lse[b, h, rows] = (m + np.log(l))[:, 0]
+    return out, lse
+
+
+def varlen_spans(cu_seqlens, total: int, max_seqlen: int):
+    """(start, length) of each packed sequence: sequence b covers rows
+    [start_b, start_b + length_b) with start_b = clamp(cu[b], 0, total),
+    end_b = clamp(cu[b + 1], start_b, total), length_b = min(end_b - start_b,
+    max_seqlen).  The offsets live on the device and cannot be checked by the
+    host, so any values give rows inside the packed tensor (reading taken
+    where the pages are silent); offsets that run backwards make spans
+    overlap, and rows shared by two sequences are then not specified."""
+    cu = np.asarray(cu_seqlens, dtype=np.int64).reshape(-1)
+    spans = []
+    for b in range(cu.shape[0] - 1):
+        start = min(max(int(cu[b]), 0), total)
+        end = min(max(int(cu[b + 1]), start), total)
+        spans.append((start, min(end - start, max_seqlen)))
+    return spans
+
+
+def attention_varlen_ref(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, *, causal=False,
+                         scale=None):
+    """Reference attention over packed variable-length sequences.
+
+    "flashrt/fa4-cute-runtime" model card, section "Functions": besides the
+    fixed-shape forward the runtime exposes FlashAttention's varlen forward,
+    in which B sequences of different lengths are packed along one token
+    dimension and delimited by cumulative offsets.  Each sequence is an
+    independent attention problem; causal is aligned bottom-right within a
+    sequence (as in attention_ref).
+
+    Args:
+      q: [total_q, Hq, D]; k, v: [total_k, Hkv, D].
+      cu_seqlens_q, cu_seqlens_k: B + 1 offsets each (spans: varlen_spans).
+      max_seqlen_q, max_seqlen_k: longest sequence; longer ones are cut.
+
+    Returns:
+      (out [total_q, Hq, D] float64, lse [Hq, total_q] float64); rows that
+      belong to no sequence are out 0 and lse -inf here (the device leaves
+      them untouched).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    total_q, Hq, D = q.shape
+    total_k = k.shape[0]
+    sq = varlen_spans(cu_seqlens_q, total_q, max_seqlen_q)
+    sk = varlen_spans(cu_seqlens_k, total_k, max_seqlen_k)
+    if len(sq) != len(sk):
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    out = np.zeros((total_q, Hq, D), dtype=np.float64)
+    lse = np.full((Hq, total_q), -np.inf, dtype=np.float64)
+    for (q0, lq), (k0, lk) in zip(sq, sk):
+        if lq == 0:
+            continue
+        if lk == 0:
+            continue  # no key: out 0, lse -inf
+        o, l = attention_ref(q[None, q0:q0 + lq], k[None, k0:k0 + lk], v[None, k0:k0 + lk], causal=causal,
+                             scale=scale)
+        out[q0:q0 + lq] = o[0]
+        lse[:, q0:q0 + lq] = l[0]
     return out, lse

@@ -12,6 +12,12 @@ AssertionError when the implementation disagrees with:
   0..i + n_b - Sq),
 * numerical stability at logits of size 1e4 (against mpmath).
 
+VARLEN_PINS do the same for the packed variable-length form
+``vimpl(q, k, v, cu_q, cu_k, max_q, max_k, causal=, scale=)``: equal
+lengths reduce to the batched form, uneven lengths agree with the brute
+force per sequence, sequences are independent, and the span rule is pinned
+by closed form.
+
 The same pins run against the oracle and against mutants of it with a
 planted mistake (tests/test_oracle_pins.py), which shows that each kind of
 plausible mistake is caught by at least one pin.
@@ -362,3 +368,92 @@ ALL_PINS = [
     pin_scale,
     pin_large_logits,
 ]
+
+
+# ------------------------------------------------------------------- varlen
+
+def _pack(rng, lens, H, D):
+    return _randn(rng, int(sum(lens)), H, D)
+
+
+def pin_varlen_equal_lengths(vimpl, batched=None):
+    """B sequences of equal lengths packed back to back: the batched
+    attention of the same tensors, causal or not."""
+    from oracle import attention_ref as batched_ref  # pinned on its own above
+    batched = batched or batched_ref
+    rng = _rng(30)
+    B, Lq, Lk, Hq, Hkv, D = 3, 4, 6, 4, 2, 5
+    for causal in (False, True):
+        q = _randn(rng, B, Lq, Hq, D)
+        k = _randn(rng, B, Lk, Hkv, D)
+        v = _randn(rng, B, Lk, Hkv, D)
+        cu_q = np.arange(B + 1) * Lq
+        cu_k = np.arange(B + 1) * Lk
+        out, lse = vimpl(q.reshape(B * Lq, Hq, D), k.reshape(B * Lk, Hkv, D), v.reshape(B * Lk, Hkv, D),
+                         cu_q, cu_k, Lq, Lk, causal=causal, scale=0.6)
+        ob, lb = batched(q, k, v, causal=causal, scale=0.6)
+        _close(out, ob.reshape(B * Lq, Hq, D), 1e-14, what=f"varlen equal lengths out causal={causal}")
+        _close(lse, lb.transpose(1, 0, 2).reshape(Hq, B * Lq), 1e-14, what=f"varlen equal lengths lse {causal}")
+
+
+def pin_varlen_brute_force(vimpl):
+    """Uneven lengths, including a sequence without queries and one without
+    keys: each sequence agrees with the mpmath brute force; rows of a
+    sequence without keys are out 0, lse -inf."""
+    rng = _rng(31)
+    lq, lk = [3, 0, 2, 4], [5, 3, 0, 2]
+    Hq, Hkv, D = 2, 1, 3
+    q, k, v = _pack(rng, lq, Hq, D), _pack(rng, lk, Hkv, D), _pack(rng, lk, Hkv, D)
+    cu_q, cu_k = np.concatenate([[0], np.cumsum(lq)]), np.concatenate([[0], np.cumsum(lk)])
+    for causal in (False, True):
+        out, lse = vimpl(q, k, v, cu_q, cu_k, max(lq), max(lk), causal=causal, scale=0.9)
+        for b in range(len(lq)):
+            qs, ks = slice(cu_q[b], cu_q[b + 1]), slice(cu_k[b], cu_k[b + 1])
+            if lq[b] == 0:
+                continue
+            if lk[b] == 0:
+                assert np.all(out[qs] == 0) and np.all(np.isneginf(lse[:, qs])), "varlen: no keys"
+                continue
+            want = brute_force(q[None, qs], k[None, ks], v[None, ks], causal=causal, scale=0.9)
+            _close(out[None, qs], want[0], 1e-12, what=f"varlen brute out seq {b} causal={causal}")
+            _close(lse[None, :, qs], want[1], 1e-12, what=f"varlen brute lse seq {b} causal={causal}")
+
+
+def pin_varlen_independence(vimpl):
+    """Changing the queries and keys of one sequence leaves the others'
+    results bit for bit."""
+    rng = _rng(32)
+    lq, lk = [3, 4, 2], [4, 5, 3]
+    q, k, v = _pack(rng, lq, 2, 4), _pack(rng, lk, 2, 4), _pack(rng, lk, 2, 4)
+    cu_q, cu_k = np.concatenate([[0], np.cumsum(lq)]), np.concatenate([[0], np.cumsum(lk)])
+    o1, l1 = vimpl(q, k, v, cu_q, cu_k, 4, 5)
+    q2, k2, v2 = q.copy(), k.copy(), v.copy()
+    q2[3:7] += 1.0
+    k2[4:9] -= 0.5
+    v2[4:9] *= 3.0
+    o2, l2 = vimpl(q2, k2, v2, cu_q, cu_k, 4, 5)
+    for sl in (slice(0, 3), slice(7, 9)):
+        assert np.array_equal(o1[sl], o2[sl]) and np.array_equal(l1[:, sl], l2[:, sl]), "varlen: sequences interact"
+    assert not np.allclose(o1[3:7], o2[3:7]), "varlen: changed sequence unchanged"
+
+
+def pin_varlen_spans(vimpl):
+    """Offsets that leave the packed tensor are clamped:
+    start = clamp(cu[b], 0, total), end = clamp(cu[b+1], start, total),
+    length = min(end - start, max_seqlen).  Checked on the result: rows in
+    no span stay out 0 / lse -inf, a sequence cut at max_seqlen equals the
+    same sequence given exactly."""
+    rng = _rng(33)
+    total_q, total_k = 9, 8
+    q, k, v = _randn(rng, total_q, 1, 3), _randn(rng, total_k, 1, 3), _randn(rng, total_k, 1, 3)
+    cu_q = np.array([-4, 2, 2, 20])   # spans: [0, 2), [2, 2) empty, [2, 9) cut to 4 rows
+    cu_k = np.array([0, 3, 5, 99])    # spans: [0, 3), [3, 5), [5, 8)
+    out, lse = vimpl(q, k, v, cu_q, cu_k, 4, 4)
+    assert np.all(out[6:] == 0) and np.all(np.isneginf(lse[:, 6:])), "varlen: rows past the cut written"
+    o_a, l_a = vimpl(q[0:2], k[0:3], v[0:3], np.array([0, 2]), np.array([0, 3]), 2, 3)
+    assert np.array_equal(out[0:2], o_a) and np.array_equal(lse[:, 0:2], l_a), "varlen: clamped first span"
+    o_c, l_c = vimpl(q[2:6], k[5:8], v[5:8], np.array([0, 4]), np.array([0, 3]), 4, 3)
+    assert np.array_equal(out[2:6], o_c) and np.array_equal(lse[:, 2:6], l_c), "varlen: span cut at max_seqlen"
+
+
+VARLEN_PINS = [pin_varlen_equal_lengths, pin_varlen_brute_force, pin_varlen_independence, pin_varlen_spans]

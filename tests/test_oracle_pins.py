@@ -21,6 +21,12 @@ def test_oracle_pin(pin):
     pin(attention_ref)
 
 
+@pytest.mark.parametrize("pin", pins.VARLEN_PINS, ids=lambda p: p.__name__)
+def test_oracle_varlen_pin(pin):
+    from oracle import attention_varlen_ref
+    pin(attention_varlen_ref)
+
+
 @settings(max_examples=25, deadline=None)
 @given(
     B=st.integers(1, 2),
@@ -71,6 +77,14 @@ MUTATIONS = [
      "s = sigma * np.matmul(q[b, :, hk, :], kb[:, hk, :].T)"),
     ("wrong batch for K", "kb = k[b, :nb]", "kb = k[0, :nb]"),
     ("seqused ignored", "nb = int(n[b])", "nb = k.shape[1]"),
+    ("varlen keys sliced by query offsets", "k[None, k0:k0 + lk], v[None, k0:k0 + lk]",
+     "k[None, q0:q0 + lk], v[None, q0:q0 + lk]"),
+    ("varlen sequences not cut at max_seqlen", "spans.append((start, min(end - start, max_seqlen)))",
+     "spans.append((start, end - start))"),
+    ("varlen negative start kept", "start = min(max(int(cu[b]), 0), total)", "start = min(int(cu[b]), total)"),
+    ("varlen lse laid out per row", "lse[:, q0:q0 + lq] = l[0]", "lse[:, q0:q0 + lq] = l[0][::-1]"),
+    ("varlen scale dropped", "causal=causal,\n                             scale=scale)",
+     "causal=causal,\n                             scale=None)"),
 ]
 
 
@@ -79,14 +93,19 @@ def _mutant(src_old, src_new):
     assert src.count(src_old) >= 1, f"mutation anchor not found: {src_old!r}"
     mod = types.ModuleType("oracle_mutant")
     exec(compile(src.replace(src_old, src_new), "oracle_mutant", "exec"), mod.__dict__)
-    return mod.attention_ref
+    return mod
 
 
-def _caught(impl):
-    for pin in pins.ALL_PINS:
+def _caught(mod):
+    runs = [(pin, mod.attention_ref) for pin in pins.ALL_PINS]
+    runs += [(pin, mod.attention_varlen_ref) for pin in pins.VARLEN_PINS]
+    for pin, impl in runs:
         try:
             with np.errstate(all="ignore"):
-                pin(impl)
+                if pin is pins.pin_varlen_equal_lengths:
+                    pin(impl, batched=mod.attention_ref)
+                else:
+                    pin(impl)
         except Exception:  # AssertionError, or the mutant crashing
             return pin.__name__
     return None
