@@ -6,14 +6,19 @@ library is loaded on first use and its absence is an error.
 """
 
 from .fa import (  # noqa: F401
+    FA_BF16,
+    FA_FP16,
     FA_OK,
     FAError,
     attention,
+    attention_varlen,
     fa_abi_version,
     fa_fwd,
     fa_fwd_plan,
+    fa_fwd_strided,
     fa_fwd_variant,
     fa_fwd_variant_workspace_bytes,
+    fa_fwd_varlen,
     fa_fwd_workspace_bytes,
     fa_set_workspace,
     fa_status_string,
@@ -21,14 +26,19 @@ from .fa import (  # noqa: F401
 )
 
 __all__ = [
+    "FA_BF16",
+    "FA_FP16",
     "FA_OK",
     "FAError",
     "attention",
+    "attention_varlen",
     "fa_abi_version",
     "fa_fwd",
     "fa_fwd_plan",
+    "fa_fwd_strided",
     "fa_fwd_variant",
     "fa_fwd_variant_workspace_bytes",
+    "fa_fwd_varlen",
     "fa_fwd_workspace_bytes",
     "fa_set_workspace",
     "fa_status_string",

@@ -250,9 +250,16 @@ int variant_plan(Plan& pl, int B, int Sq, int Sk, int Hq, int Hkv, int D, int ca
   return FA_OK;
 }
 
+// A packed variable-length batch (fa_fwd_varlen): device offsets and row counts.
+struct Packed {
+  const int32_t* cu_q = nullptr;
+  const int32_t* cu_k = nullptr;
+  int total_q = 0, total_k = 0;
+};
+
 int run(const Plan& pl, const void* q, const void* k, const void* v, void* out, float* lse, int B, int Sq,
         int Sk, int Hq, int Hkv, const View& vq, const View& vk, const View& vv, const View& vo,
-        const int32_t* seqused_k, float scale, hipStream_t stream) {
+        const int32_t* seqused_k, float scale, hipStream_t stream, const Packed& packed = Packed()) {
   fa::FwdParams p{};
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k);
@@ -268,6 +275,17 @@ int run(const Plan& pl, const void* q, const void* k, const void* v, void* out, 
   p.g = Hq / Hkv;
   p.Mp = pl.Mp;
   p.coff = Sk - Sq;
+  p.lse_hs = Sq;
+  if (packed.cu_q != nullptr) {
+    p.cu_q = packed.cu_q;
+    p.cu_k = packed.cu_k;
+    p.total_q = packed.total_q;
+    p.total_k = packed.total_k;
+    p.lse_hs = packed.total_q;
+    // Grids are planned for the longest sequences; a sequence may pair any
+    // query count with up to Sk keys, so causal blocks plan for all Sk keys.
+    p.coff = Sk - 1;
+  }
   p.kps = pl.kps;
   p.nrb = pl.nrb;
   p.zmax = pl.zmax;
@@ -362,6 +380,45 @@ int fa_fwd_strided(const void* q, const void* k, const void* v, void* out, float
   if (!fa::variant_exists(D, pl.launch.qt, pl.launch.nw, pl.launch.kw, pl.launch.bn, pl.launch.nst, dtype))
     return FA_ERR_UNSUPPORTED;
   return run(pl, q, k, v, out, lse, B, Sq, Sk, Hq, Hkv, vq, vk, vv, vo, seqused_k, scale, stream);
+}
+
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse, const int32_t* cu_seqlens_q,
+                  const int32_t* cu_seqlens_k, int B, int max_seqlen_q, int max_seqlen_k, int total_q, int total_k,
+                  int Hq, int Hkv, int D, int dtype, int causal, float scale, hipStream_t stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || cu_seqlens_q == nullptr ||
+      cu_seqlens_k == nullptr)
+    return FA_ERR_NULL;
+  if (B < 1 || max_seqlen_q < 1 || max_seqlen_k < 1 || total_q < 1 || total_k < 1 || Hq < 1 || Hkv < 1 || D < 1 ||
+      Hq % Hkv != 0 || (causal != 0 && causal != 1))
+    return FA_ERR_SHAPE;
+  if ((long long)B * Hkv > 65535 || (long long)max_seqlen_q * (Hq / Hkv) > INT32_MAX / 2) return FA_ERR_SHAPE;
+  if ((long long)total_q * Hq * D > INT32_MAX || (long long)total_k * Hkv * D > INT32_MAX) return FA_ERR_SHAPE;
+  if ((long long)max_seqlen_k * Hkv * D * 2 >= (1ll << 31)) return FA_ERR_SHAPE;
+  if (!supported_d(D)) return FA_ERR_UNSUPPORTED;
+  if (dtype != fa::kBf16 && dtype != fa::kF16) return FA_ERR_UNSUPPORTED;
+  if (!(scale > 0.0f) || !isfinite(scale)) return FA_ERR_SCALE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return FA_ERR_ALIGN;
+  if ((lse != nullptr && !aligned(lse, 4)) || !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4))
+    return FA_ERR_ALIGN;
+  const size_t qb = (size_t)total_q * Hq * D * 2, kb = (size_t)total_k * Hkv * D * 2;
+  if (overlap(out, qb, q, qb) || overlap(out, qb, k, kb) || overlap(out, qb, v, kb)) return FA_ERR_ALIAS;
+  if (lse != nullptr) {
+    const size_t lb = (size_t)Hq * total_q * sizeof(float);
+    if (overlap(lse, lb, q, qb) || overlap(lse, lb, k, kb) || overlap(lse, lb, v, kb) || overlap(lse, lb, out, qb))
+      return FA_ERR_ALIAS;
+  }
+  Plan pl = default_plan(B, max_seqlen_q, max_seqlen_k, Hq, Hkv, D, causal);
+  pl.launch.dtype = dtype;
+  if (!fa::variant_exists(D, pl.launch.qt, pl.launch.nw, pl.launch.kw, pl.launch.bn, pl.launch.nst, dtype))
+    return FA_ERR_UNSUPPORTED;
+  Packed packed;
+  packed.cu_q = cu_seqlens_q;
+  packed.cu_k = cu_seqlens_k;
+  packed.total_q = total_q;
+  packed.total_k = total_k;
+  const View vq{0, (long long)Hq * D, D}, vk{0, (long long)Hkv * D, D};
+  return run(pl, q, k, v, out, lse, B, max_seqlen_q, max_seqlen_k, Hq, Hkv, vq, vk, vk, vq, nullptr, scale, stream,
+             packed);
 }
 
 int fa_fwd_variant(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Sq, int Sk,

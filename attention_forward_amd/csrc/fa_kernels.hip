@@ -504,6 +504,42 @@ __host__ __device__ __forceinline__ int causal_kmax(int rb, int rows, int Mp, in
   return k < 0 ? 0 : (k > Sk ? Sk : k);
 }
 
+// Rows and keys of batch entry b.  Fixed shape: query positions 0..Sq-1
+// and keys 0..n-1, n from seqused_k.  Packed variable-length batch: the
+// b-th sequence, its offsets read on the device and clamped into the
+// tensors (start in [0, total], end in [start, total], length at most the
+// planned maximum), so any values stay in bounds.
+struct Seq {
+  int q0, sq;       // first query position, query count
+  int k0, nk;       // first key position, attended key count
+  long long lse0;   // lse index of (head 0, query 0); heads are p.lse_hs apart
+};
+
+__device__ __forceinline__ Seq seq_of(const FwdParams& p, int b) {
+  Seq r;
+  if (p.cu_q != nullptr) {
+    int a = min(max(p.cu_q[b], 0), p.total_q), e = min(max(p.cu_q[b + 1], a), p.total_q);
+    r.q0 = a;
+    r.sq = min(e - a, p.Sq);
+    a = min(max(p.cu_k[b], 0), p.total_k);
+    e = min(max(p.cu_k[b + 1], a), p.total_k);
+    r.k0 = a;
+    r.nk = min(e - a, p.Sk);
+  } else {
+    r.q0 = 0;
+    r.sq = p.Sq;
+    r.k0 = 0;
+    r.nk = p.seqused != nullptr ? min(max(p.seqused[b], 0), p.Sk) : p.Sk;
+  }
+  // uniform per workgroup: keeps buffer resources and loop bounds scalar
+  r.q0 = __builtin_amdgcn_readfirstlane(r.q0);
+  r.sq = __builtin_amdgcn_readfirstlane(r.sq);
+  r.k0 = __builtin_amdgcn_readfirstlane(r.k0);
+  r.nk = __builtin_amdgcn_readfirstlane(r.nk);
+  r.lse0 = p.cu_q != nullptr ? (long long)r.q0 : (long long)b * p.Hq * p.Sq;
+  return r;
+}
+
 struct RowBlock {
   int rb;      // row block index
   int z;       // key chunk (split) index
@@ -532,9 +568,9 @@ fwd_kernel(const FwdParams p) {
   const int b = bh / p.Hkv, hk = bh - b * p.Hkv;
   const int g = p.g;
 
-  int nvalid = p.Sk;
-  if (p.seqused != nullptr) nvalid = min(max(p.seqused[b], 0), p.Sk);
-  nvalid = __builtin_amdgcn_readfirstlane(nvalid);  // uniform: keeps the buffer resources in SGPRs
+  const Seq sq = seq_of(p, b);
+  const int nvalid = sq.nk;
+  const int Mp = sq.sq * g;  // packed rows of this batch entry (the grid covers the planned maximum)
 
   // Which rows and keys this workgroup takes.
   RowBlock blk;
@@ -554,7 +590,7 @@ fwd_kernel(const FwdParams p) {
     blk.kbeg = SPLIT ? item * p.kps : 0;
     blk.kend = SPLIT ? min(blk.kbeg + p.kps, kmax) : kmax;
     // the valid keys, up to the diagonal of the block's last row
-    blk.kend = min(min(blk.kend, nvalid), (min((rb + 1) * G::ROWS_WG, p.Mp) - 1) / g + (nvalid - p.Sq) + 1);
+    blk.kend = min(min(blk.kend, nvalid), (min((rb + 1) * G::ROWS_WG, Mp) - 1) / g + (nvalid - sq.sq) + 1);
   } else {
     blk.rb = rb_x;
     blk.z = SPLIT ? blockIdx.z : 0;
@@ -562,17 +598,18 @@ fwd_kernel(const FwdParams p) {
     blk.kend = SPLIT ? min(blk.kbeg + p.kps, nvalid) : nvalid;
   }
   const int row0 = blk.rb * G::ROWS_WG;
+  if (row0 >= Mp) return;  // past a shorter sequence of a packed batch: nothing to do
   const int rw0 = row0 + wave * 16 * QT;
   const int kbeg = blk.kbeg, kend = blk.kend;
 
   typename G::E::v8 qf[QT][G::KC];
   int srow[QT];
-  const bool wave_active = rw0 < p.Mp;
+  const bool wave_active = rw0 < Mp;
   // Causal: diagonal keys (last attended key) of the wave's first and last
   // rows; the last query lines up with the last valid key.
-  const int doff = CAUSAL ? nvalid - p.Sq : 0;
-  const int s_lo = min(rw0, p.Mp - 1) / g + doff;
-  const int s_hi = (min(rw0 + 16 * QT, p.Mp) - 1) / g + doff;
+  const int doff = CAUSAL ? nvalid - sq.sq : 0;
+  const int s_lo = min(rw0, Mp - 1) / g + doff;
+  const int s_hi = (min(rw0 + 16 * QT, Mp) - 1) / g + doff;
 
   f32x4_t oacc[G::DT][QT];
 #pragma unroll
@@ -590,8 +627,8 @@ fwd_kernel(const FwdParams p) {
   // ---- K/V tile copies.  Buffers start at this (batch, kv head)'s first key
   // and end after key kend - 1, so every key at or past kend reads as zero.
   const uint32_t rstride_k = (uint32_t)(p.k_ss * 2), rstride_v = (uint32_t)(p.v_ss * 2);  // bytes between keys
-  const u32x4_t rk = make_rsrc(p.k + b * p.k_sb + hk * p.k_sh, (uint32_t)kend * rstride_k);
-  const u32x4_t rv = make_rsrc(p.v + b * p.v_sb + hk * p.v_sh, (uint32_t)kend * rstride_v);
+  const u32x4_t rk = make_rsrc(p.k + b * p.k_sb + sq.k0 * p.k_ss + hk * p.k_sh, (uint32_t)kend * rstride_k);
+  const u32x4_t rv = make_rsrc(p.v + b * p.v_sb + sq.k0 * p.v_ss + hk * p.v_sh, (uint32_t)kend * rstride_v);
   // Per-thread source offsets of its slots within a tile: slot P holds row
   // P / (STR/16), chunk P % (STR/16); padding chunks and trash windows read
   // out of range (zeros, no memory access).
@@ -663,11 +700,11 @@ fwd_kernel(const FwdParams p) {
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
     const int r = rw0 + 16 * t + col;
-    const bool ok = r < p.Mp;
+    const bool ok = r < Mp;
     const int s = ok ? r / g : 0;
     const int hh = ok ? r - s * g : 0;
     srow[t] = ok ? s + doff : -1;  // causal: the row's diagonal key
-    const uint16_t* qp = p.q + b * p.q_sb + s * p.q_ss + (hk * g + hh) * p.q_sh;
+    const uint16_t* qp = p.q + b * p.q_sb + (sq.q0 + s) * p.q_ss + (hk * g + hh) * p.q_sh;
 #pragma unroll
     for (int c = 0; c < G::KC; ++c) {
       const int d0 = 32 * c + 8 * grp;
@@ -748,11 +785,11 @@ fwd_kernel(const FwdParams p) {
 #pragma unroll
     for (int t = 0; t < QT; ++t) {
       const int r = rw0 + 16 * t + col;
-      if (r >= p.Mp) continue;
+      if (r >= Mp) continue;
       const int s = r / g, hh = r - s * g;
       const float l = l_tot[t];
       const float inv = (l > 0.f) ? 1.0f / l : 0.f;
-      uint16_t* op = p.out + b * p.o_sb + s * p.o_ss + (hk * g + hh) * p.o_sh;
+      uint16_t* op = p.out + b * p.o_sb + (sq.q0 + s) * p.o_ss + (hk * g + hh) * p.o_sh;
 #pragma unroll
       for (int dt = 0; dt < G::DT; ++dt) {
         const int d = 16 * dt + 4 * grp;
@@ -764,7 +801,7 @@ fwd_kernel(const FwdParams p) {
       }
       if (p.lse != nullptr && grp == 0) {
         const float lse = (l > 0.f) ? (m_run[t] + __log2f(l)) * kLn2 : -INFINITY;
-        p.lse[((size_t)b * p.Hq + hk * g + hh) * p.Sq + s] = lse;
+        p.lse[sq.lse0 + (long long)(hk * g + hh) * p.lse_hs + s] = lse;
       }
     }
   } else {
@@ -774,7 +811,7 @@ fwd_kernel(const FwdParams p) {
 #pragma unroll
     for (int t = 0; t < QT; ++t) {
       const int rl = wave * 16 * QT + 16 * t + col;  // row within the block
-      if (row0 + rl >= p.Mp) continue;
+      if (row0 + rl >= Mp) continue;
       const size_t prow = (slot_base + blk.z) * G::ROWS_WG + rl;
       const float l = l_tot[t];
       const float inv = (l > 0.f) ? 1.0f / l : 0.f;
@@ -827,9 +864,9 @@ fwd_ks_kernel(const FwdParams p) {
   const int b = bh / p.Hkv, hk = bh - b * p.Hkv;
   const int g = p.g;
 
-  int nvalid = p.Sk;
-  if (p.seqused != nullptr) nvalid = min(max(p.seqused[b], 0), p.Sk);
-  nvalid = __builtin_amdgcn_readfirstlane(nvalid);
+  const Seq sq = seq_of(p, b);
+  const int nvalid = sq.nk;
+  const int Mp = sq.sq * g;  // packed rows of this batch entry (the grid covers the planned maximum)
 
   RowBlock blk;
   if constexpr (CAUSAL) {
@@ -847,7 +884,7 @@ fwd_ks_kernel(const FwdParams p) {
     blk.kbeg = SPLIT ? item * p.kps : 0;
     blk.kend = SPLIT ? min(blk.kbeg + p.kps, kmax) : kmax;
     // the valid keys, up to the diagonal of the block's last row
-    blk.kend = min(min(blk.kend, nvalid), (min((rb + 1) * ROWS, p.Mp) - 1) / g + (nvalid - p.Sq) + 1);
+    blk.kend = min(min(blk.kend, nvalid), (min((rb + 1) * ROWS, Mp) - 1) / g + (nvalid - sq.sq) + 1);
   } else {
     blk.rb = blockIdx.x;
     blk.z = SPLIT ? blockIdx.z : 0;
@@ -855,9 +892,10 @@ fwd_ks_kernel(const FwdParams p) {
     blk.kend = SPLIT ? min(blk.kbeg + p.kps, nvalid) : nvalid;
   }
   const int row0 = blk.rb * ROWS;
+  if (row0 >= Mp) return;  // past a shorter sequence of a packed batch: nothing to do
   const int kbeg = blk.kbeg, kend = blk.kend;
-  const int doff = CAUSAL ? nvalid - p.Sq : 0;  // causal: diagonal key offset (last query <-> last valid key)
-  const int s_lo = min(row0, p.Mp - 1) / g + doff;
+  const int doff = CAUSAL ? nvalid - sq.sq : 0;  // causal: diagonal key offset (last query <-> last valid key)
+  const int s_lo = min(row0, Mp - 1) / g + doff;
 
   typename G::E::v8 qf[QT][G::KC];
   int srow[QT];
@@ -876,8 +914,8 @@ fwd_ks_kernel(const FwdParams p) {
 
   // ---- this wave's K/V copies (see fwd_kernel: out-of-range keys read as 0)
   const uint32_t rstride_k = (uint32_t)(p.k_ss * 2), rstride_v = (uint32_t)(p.v_ss * 2);
-  const u32x4_t rk = make_rsrc(p.k + b * p.k_sb + hk * p.k_sh, (uint32_t)kend * rstride_k);
-  const u32x4_t rv = make_rsrc(p.v + b * p.v_sb + hk * p.v_sh, (uint32_t)kend * rstride_v);
+  const u32x4_t rk = make_rsrc(p.k + b * p.k_sb + sq.k0 * p.k_ss + hk * p.k_sh, (uint32_t)kend * rstride_k);
+  const u32x4_t rv = make_rsrc(p.v + b * p.v_sb + sq.k0 * p.v_ss + hk * p.v_sh, (uint32_t)kend * rstride_v);
   uint32_t voff_k[G::LPT_K], voff_v[G::LPT_V];
 #pragma unroll
   for (int j = 0; j < G::LPT_K; ++j) {
@@ -920,9 +958,9 @@ fwd_ks_kernel(const FwdParams p) {
   // padding read as zeros.
   {
     const int s_first = row0 / g;
-    const int s_last = (min(row0 + ROWS, p.Mp) - 1) / g;
+    const int s_last = (min(row0 + ROWS, Mp) - 1) / g;
     const uint32_t qrow_b = (uint32_t)(p.q_ss * 2), qhead_b = (uint32_t)(p.q_sh * 2);
-    const u32x4_t rq = make_rsrc(p.q + b * p.q_sb + s_first * p.q_ss + hk * g * p.q_sh,
+    const u32x4_t rq = make_rsrc(p.q + b * p.q_sb + (sq.q0 + s_first) * p.q_ss + hk * g * p.q_sh,
                                  (uint32_t)(s_last - s_first) * qrow_b + (uint32_t)(g - 1) * qhead_b + D * 2);
     const uint32_t lds_q = (uint32_t)(uintptr_t)(lds_void_t*)(smem + Q_OFF);
     for (int j = wave; j < Q_INSTR; j += KW) {
@@ -930,7 +968,7 @@ fwd_ks_kernel(const FwdParams p) {
       const int row = P / (G::KSTR / 16), ch = P - row * (G::KSTR / 16);
       const int r = row0 + row;
       uint32_t off = kOutOfRange;
-      if (row < ROWS && ch < G::CPR && r < p.Mp) {
+      if (row < ROWS && ch < G::CPR && r < Mp) {
         const int sq = r / g;
         off = (uint32_t)(sq - s_first) * qrow_b + (uint32_t)(r - sq * g) * qhead_b + (uint32_t)(ch * 16);
       }
@@ -954,7 +992,7 @@ fwd_ks_kernel(const FwdParams p) {
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
     const int r = row0 + 16 * t + col;
-    srow[t] = r < p.Mp ? r / g + doff : -1;  // causal: the row's diagonal key
+    srow[t] = r < Mp ? r / g + doff : -1;  // causal: the row's diagonal key
 #pragma unroll
     for (int c = 0; c < G::KC; ++c) {
       qf[t][c] = G::E::cast(*reinterpret_cast<const u32x4_t*>(smem + Q_OFF + (16 * t + col) * G::KSTR + c * 64 + grp * 16));
@@ -1009,7 +1047,7 @@ fwd_ks_kernel(const FwdParams p) {
   static_assert(TPR * ROWS == KW * 64, "whole rows per workgroup pass");
   const int rl = tid / TPR, c0 = tid - rl * TPR;
   const int r = row0 + rl;
-  if (r < p.Mp) {
+  if (r < Mp) {
     float mw[KW], fw[KW];
     float M = -INFINITY;
 #pragma unroll
@@ -1043,7 +1081,7 @@ fwd_ks_kernel(const FwdParams p) {
         if constexpr (!SPLIT) {
           const u32x4_t o = {G::E::pack(a0[0], a0[1]), G::E::pack(a0[2], a0[3]), G::E::pack(a1[0], a1[1]),
                              G::E::pack(a1[2], a1[3])};
-          *reinterpret_cast<u32x4_t*>(p.out + b * p.o_sb + s * p.o_ss + (hk * g + hh) * p.o_sh + 8 * ch) = o;
+          *reinterpret_cast<u32x4_t*>(p.out + b * p.o_sb + (sq.q0 + s) * p.o_ss + (hk * g + hh) * p.o_sh + 8 * ch) = o;
         } else {
           const size_t prow = (((size_t)bh * p.nrb + blk.rb) * p.zmax + blk.z) * ROWS + rl;
           float* po = p.ws_o + prow * D + 8 * ch;
@@ -1055,7 +1093,7 @@ fwd_ks_kernel(const FwdParams p) {
     if (c0 == 0) {
       if constexpr (!SPLIT) {
         if (p.lse != nullptr)
-          p.lse[((size_t)b * p.Hq + hk * g + hh) * p.Sq + s] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : -INFINITY;
+          p.lse[sq.lse0 + (long long)(hk * g + hh) * p.lse_hs + s] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : -INFINITY;
       } else {
         const size_t prow = (((size_t)bh * p.nrb + blk.rb) * p.zmax + blk.z) * ROWS + rl;
         *reinterpret_cast<u32x2_t*>(p.ws_ml + 2 * prow) = u32x2_t{__float_as_uint(M), __float_as_uint(L)};
@@ -1083,9 +1121,10 @@ combine_kernel(const FwdParams p) {
   const int rl = (rem / CPR) % ROWS_WG;
   const int ch = rem % CPR;
   const int r = rb * ROWS_WG + rl;
-  if (r >= p.Mp) return;
   const int g = p.g;
   const int b = bh / p.Hkv, hk = bh - b * p.Hkv;
+  const Seq sq = seq_of(p, b);
+  if (r >= sq.sq * g) return;  // past the end of this batch entry's queries
   int nz = p.zmax;
   if constexpr (CAUSAL) {
     nz = (causal_kmax(rb, ROWS_WG, p.Mp, g, p.coff, p.Sk) + p.kps - 1) / p.kps;
@@ -1124,10 +1163,10 @@ combine_kernel(const FwdParams p) {
   const float inv = (L > 0.f) ? 1.0f / L : 0.f;
   const u32x4_t o = {E::pack(a0[0] * inv, a0[1] * inv), E::pack(a0[2] * inv, a0[3] * inv),
                      E::pack(a1[0] * inv, a1[1] * inv), E::pack(a1[2] * inv, a1[3] * inv)};
-  *reinterpret_cast<u32x4_t*>(p.out + b * p.o_sb + s * p.o_ss + (hk * g + hh) * p.o_sh + 8 * ch) = o;
+  *reinterpret_cast<u32x4_t*>(p.out + b * p.o_sb + (sq.q0 + s) * p.o_ss + (hk * g + hh) * p.o_sh + 8 * ch) = o;
   if (ch == 0 && p.lse != nullptr) {
     const float lse = (L > 0.f) ? (M + __log2f(L)) * kLn2 : -INFINITY;
-    p.lse[((size_t)b * p.Hq + hk * g + hh) * p.Sq + s] = lse;
+    p.lse[sq.lse0 + (long long)(hk * g + hh) * p.lse_hs + s] = lse;
   }
 }
 

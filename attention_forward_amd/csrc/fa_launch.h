@@ -15,6 +15,13 @@ struct FwdParams {
   uint16_t* out;           // (batch, position, head, head_dim) view, written
   float* lse;              // [B, Hq, Sq] fp32 contiguous, or null
   const int32_t* seqused;  // [B] int32 on the device, or null
+  // Packed variable-length batch (both null otherwise): B + 1 offsets each,
+  // on the device, of the sequences along the token dimension of q / out
+  // and of k / v (whose batch strides are then 0).
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int total_q, total_k;    // token rows of q / out and of k / v (packed batch)
+  long long lse_hs;        // lse elements between heads: Sq, or total_q for a packed batch
   // Split-KV workspace (split variants only).  Partial rows are indexed
   // ((bh * nrb + row_block) * zmax + split) * rows_per_block + row_in_block.
   float* ws_o;             // partial O / l, fp32, D per partial row

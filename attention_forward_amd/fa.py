@@ -33,7 +33,7 @@ FA_ERR_ALIAS = 8
 FA_BF16 = 0
 FA_FP16 = 1
 
-EXPORTS = ("fa_fwd", "fa_fwd_strided", "fa_fwd_workspace_bytes", "fa_set_workspace", "fa_fwd_variant",
+EXPORTS = ("fa_fwd", "fa_fwd_strided", "fa_fwd_varlen", "fa_fwd_workspace_bytes", "fa_set_workspace", "fa_fwd_variant",
            "fa_fwd_variant_workspace_bytes", "fa_fwd_plan", "fa_status_string", "fa_abi_version")
 
 _lib = None
@@ -65,6 +65,8 @@ def load_library():
         i64 = ctypes.c_int64
         lib.fa_fwd_strided.restype = i32
         lib.fa_fwd_strided.argtypes = [vp, vp, vp, vp, vp] + [i32] * 6 + [i64] * 12 + [i32, i32, vp, f32, vp]
+        lib.fa_fwd_varlen.restype = i32
+        lib.fa_fwd_varlen.argtypes = [vp] * 7 + [i32] * 10 + [f32, vp]
         lib.fa_fwd_workspace_bytes.restype = ctypes.c_size_t
         lib.fa_fwd_workspace_bytes.argtypes = [i32] * 7
         lib.fa_set_workspace.restype = i32
@@ -102,6 +104,15 @@ def fa_fwd_strided(q, k, v, out, lse, B, Sq, Sk, Hq, Hkv, D, q_strides, k_stride
     return load_library().fa_fwd_strided(q or None, k or None, v or None, out or None, lse or None,
                                          B, Sq, Sk, Hq, Hkv, D, *st, int(dtype), int(causal),
                                          seqused_k or None, ctypes.c_float(scale), stream or None)
+
+
+def fa_fwd_varlen(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, B, max_seqlen_q, max_seqlen_k, total_q, total_k,
+                  Hq, Hkv, D, dtype, causal, scale, stream) -> int:
+    """C ``fa_fwd_varlen``; pointers and stream are integers (0 for NULL)."""
+    return load_library().fa_fwd_varlen(q or None, k or None, v or None, out or None, lse or None,
+                                        cu_seqlens_q or None, cu_seqlens_k or None, B, max_seqlen_q, max_seqlen_k,
+                                        total_q, total_k, Hq, Hkv, D, int(dtype), int(causal),
+                                        ctypes.c_float(scale), stream or None)
 
 
 def fa_fwd_workspace_bytes(B, Sq, Sk, Hq, Hkv, D, causal) -> int:
@@ -235,4 +246,61 @@ def attention(q, k, v, *, causal=False, seqused_k=None, scale=None, out=None, ls
             where = "fa_fwd_strided"
     if rc != FA_OK:
         raise FAError(rc, where)
+    return out, lse
+
+
+def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, *, causal=False,
+                     scale=None, out=None, lse=None, return_lse=True):
+    """Attention over packed variable-length sequences (fa_fwd_varlen).
+
+    q [total_q, Hq, D], k and v [total_k, Hkv, D], contiguous, one dtype
+    (bfloat16 or float16); cu_seqlens_q / cu_seqlens_k contiguous int32
+    [B + 1] on q's device; max_seqlen_q / max_seqlen_k host ints bounding the
+    sequence lengths.  Returns (out [total_q, Hq, D], lse [Hq, total_q]
+    float32 or None).  A passed ``out`` keeps the values of rows that belong
+    to no sequence.
+    """
+    import torch
+
+    dtypes = {torch.bfloat16: FA_BF16, torch.float16: FA_FP16}
+    if not isinstance(q, torch.Tensor) or q.dtype not in dtypes or not q.is_cuda:
+        raise TypeError("q must be a bfloat16 or float16 cuda tensor")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.dtype != q.dtype or t.device != q.device:
+            raise TypeError(f"{name} must be a tensor of q's dtype on q's device")
+        if t.dim() != 3 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 3-D (tokens, heads, head_dim) tensor")
+    total_q, Hq, D = q.shape
+    total_k, Hkv, Dk = k.shape
+    if tuple(v.shape) != tuple(k.shape) or Dk != D:
+        raise ValueError("k and v must be [total_k, Hkv, D] matching q")
+    dev = q.device
+    for name, c in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if not isinstance(c, torch.Tensor) or c.dtype != torch.int32 or c.device != dev or c.dim() != 1 \
+                or not c.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous int32 vector on q's device")
+    if cu_seqlens_q.numel() != cu_seqlens_k.numel() or cu_seqlens_q.numel() < 2:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k need the same B + 1 >= 2 entries")
+    B = cu_seqlens_q.numel() - 1
+    if out is None:
+        out = torch.empty_like(q)
+    elif tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype or out.device != dev or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor shaped and typed like q")
+    if lse is None and return_lse:
+        lse = torch.empty((Hq, total_q), dtype=torch.float32, device=dev)
+    elif lse is not None and (tuple(lse.shape) != (Hq, total_q) or lse.dtype != torch.float32
+                              or lse.device != dev or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 [Hq, total_q] tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    causal = bool(causal)
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        ensure_workspace(dev, fa_fwd_workspace_bytes(B, int(max_seqlen_q), int(max_seqlen_k), Hq, Hkv, D, causal))
+        rc = fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                           0 if lse is None else lse.data_ptr(), cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(),
+                           B, int(max_seqlen_q), int(max_seqlen_k), total_q, total_k, Hq, Hkv, D, dtypes[q.dtype],
+                           causal, float(scale), stream)
+    if rc != FA_OK:
+        raise FAError(rc, "fa_fwd_varlen")
     return out, lse

@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 2
+#define FA_ABI_VERSION 3
 
 /* Status codes. */
 enum {
@@ -136,6 +136,40 @@ int fa_fwd_strided(const void* q, const void* k, const void* v, void* out, float
                    int64_t v_sb, int64_t v_ss, int64_t v_sh,
                    int64_t o_sb, int64_t o_ss, int64_t o_sh,
                    int dtype, int causal, const int32_t* seqused_k, float scale, hipStream_t stream);
+
+/* fa_fwd_varlen: attention over a packed batch of variable-length
+ * sequences, the varlen forward listed beside the fixed-shape one in the
+ * "flashrt/fa4-cute-runtime" card, section "Functions" (multi-view or
+ * multi-request packing without padding).
+ *
+ *   q, out        [total_q, Hq, D] contiguous, the B sequences' queries back
+ *                 to back; out rows that belong to no sequence are not written
+ *   k, v          [total_k, Hkv, D] contiguous, the sequences' keys
+ *   lse           [Hq, total_q] fp32 (natural log, scale included), or NULL
+ *   cu_seqlens_q, cu_seqlens_k
+ *                 int32[B + 1] on the DEVICE: sequence b has the query rows
+ *                 [cu_q[b], cu_q[b+1]) and the keys [cu_k[b], cu_k[b+1]).
+ *                 Meant to be non-decreasing from 0; the kernels clamp every
+ *                 span into its tensor (start to [0, total], end to
+ *                 [start, total]) and cut it at max_seqlen, so no value can
+ *                 address memory outside the tensors (spans that overlap
+ *                 because the offsets run backwards give unspecified rows).
+ *   max_seqlen_q, max_seqlen_k
+ *                 host bounds on the span lengths; the grid is planned for
+ *                 them (and the kernel variant is fa_fwd_plan's for
+ *                 B, max_seqlen_q, max_seqlen_k)
+ *   dtype         FA_BF16 or FA_FP16
+ *   causal        as for fa_fwd within each sequence: query i of a sequence
+ *                 with n keys attends keys j <= i + (n - its query count)
+ *   A sequence without keys gives out = 0 and lse = -inf on its rows.
+ * Workspace: fa_fwd_workspace_bytes(B, max_seqlen_q, max_seqlen_k, Hq, Hkv,
+ * D, causal).  Checks and codes as for fa_fwd (sizes: total_q*Hq*D and
+ * total_k*Hkv*D elements and max_seqlen_k*Hkv*D*2 bytes below 2^31;
+ * cu_seqlens 4-byte aligned; out/lse must not overlap q, k, v). */
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
+                  const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                  int B, int max_seqlen_q, int max_seqlen_k, int total_q, int total_k,
+                  int Hq, int Hkv, int D, int dtype, int causal, float scale, hipStream_t stream);
 
 /* Bytes of workspace fa_fwd needs for this shape (0: none).  Pure host
  * arithmetic; returns 0 for invalid shapes as well.  The same figure holds

@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert fa.fa_abi_version() == 2
+    assert fa.fa_abi_version() == 3
     for code in range(9):
         assert fa.fa_status_string(code).startswith("FA_")
     assert "UNKNOWN" in fa.fa_status_string(99)
@@ -131,6 +131,41 @@ def _call_strided(qs=None, ks=None, vs=None, os_=None, dtype=fa.FA_BF16, **over)
 ])
 def test_strided_invalid_arguments_return_their_code(lib, over, code):
     assert _call_strided(**over) == code
+
+
+def _call_varlen(**over):
+    a = dict(q=Q, k=K, v=V, out=O, lse=L, cu_q=S, cu_k=S + 64, B=2, max_q=64, max_k=64, total_q=100,
+             total_k=100, Hq=8, Hkv=1, D=256, dtype=fa.FA_BF16, causal=0, scale=0.0625, stream=0)
+    a.update(over)
+    return fa.fa_fwd_varlen(a["q"], a["k"], a["v"], a["out"], a["lse"], a["cu_q"], a["cu_k"], a["B"], a["max_q"],
+                            a["max_k"], a["total_q"], a["total_k"], a["Hq"], a["Hkv"], a["D"], a["dtype"],
+                            a["causal"], a["scale"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=0), fa.FA_ERR_NULL),
+    (dict(cu_q=0), fa.FA_ERR_NULL),
+    (dict(cu_k=0), fa.FA_ERR_NULL),
+    (dict(B=0), fa.FA_ERR_SHAPE),
+    (dict(max_q=0), fa.FA_ERR_SHAPE),
+    (dict(max_k=0), fa.FA_ERR_SHAPE),
+    (dict(total_q=0), fa.FA_ERR_SHAPE),
+    (dict(Hq=6, Hkv=4), fa.FA_ERR_SHAPE),
+    (dict(causal=3), fa.FA_ERR_SHAPE),
+    (dict(B=70000, Hkv=1), fa.FA_ERR_SHAPE),
+    (dict(total_q=1 << 24), fa.FA_ERR_SHAPE),
+    (dict(max_k=1 << 22), fa.FA_ERR_SHAPE),
+    (dict(D=128), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=5), fa.FA_ERR_UNSUPPORTED),
+    (dict(scale=-1.0), fa.FA_ERR_SCALE),
+    (dict(k=K + 8), fa.FA_ERR_ALIGN),
+    (dict(cu_q=S + 2), fa.FA_ERR_ALIGN),
+    (dict(lse=L + 1), fa.FA_ERR_ALIGN),
+    (dict(out=Q + 1024), fa.FA_ERR_ALIAS),
+    (dict(lse=O + 4096), fa.FA_ERR_ALIAS),
+])
+def test_varlen_invalid_arguments_return_their_code(lib, over, code):
+    assert _call_varlen(**over) == code
 
 
 def test_check_order_is_null_then_shape(lib):
