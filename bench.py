@@ -325,6 +325,74 @@ def ingest_traffic(workload, fetch_csv, write_csv, out_path=TRAFFIC_FILE):
     return entry
 
 
+def extension_rows(device, steps=200):
+    """µs per call of the extended entry points on shapes taken from the
+    workloads: fp16, a fused QKV buffer read in place, a packed
+    variable-length batch, a causal chunk of new positions attending a cache,
+    and causal decode over the padded prefix cache."""
+    import torch
+    from attention_forward_amd import fa
+    from attention_forward_amd.workloads import make_custom
+
+    rows = {}
+
+    def record(name, launch, flops, nbytes):
+        _, ev = time_graph(launch, steps, 5, device)
+        s = ev / steps
+        rows[name] = {"us_per_call": round(s * 1e6, 3), "tflops": round(flops / s / 1e12, 3),
+                      "gbs": round(nbytes / s / 1e9, 2)}
+
+    def pairs_causal(sq, n, h):
+        return h * sum(max(0, min(i + 1 + n - sq, n)) for i in range(sq))
+
+    B, S, H, D = 3, 256, 16, 72
+    vit_flops, vit_bytes = 4 * D * B * H * S * S, 4 * B * S * H * D * 2 + B * H * S * 4
+    # fp16 ViT (contiguous, through fa_fwd_strided)
+    q, k, v, _ = make_custom(B, S, S, H, H, D, seed=2, dtype=torch.float16)
+    q, k, v = (t.to(device) for t in (q, k, v))
+    out, lse = torch.empty_like(q), torch.empty(B, H, S, dtype=torch.float32, device=device)
+    st = (S * H * D, H * D, D)
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, S, S, H, H, D, st, st, st,
+            st, fa.FA_FP16, 0, 0, 1.0 / math.sqrt(D))
+    record("vit_multiview_fp16", lambda h, a=args: fa.fa_fwd_strided(*a, h), vit_flops, vit_bytes)
+    # ViT read from a fused [B, S, 3H, D] QKV buffer (bf16 views)
+    qkv = torch.randn(B, S, 3 * H, D, device=device).to(torch.bfloat16)
+    out = torch.empty(B, S, H, D, dtype=torch.bfloat16, device=device)
+    fs = (S * 3 * H * D, 3 * H * D, D)
+    base = qkv.data_ptr()
+    args = (base, base + H * D * 2, base + 2 * H * D * 2, out.data_ptr(), lse.data_ptr(), B, S, S, H, H, D, fs, fs,
+            fs, st, fa.FA_BF16, 0, 0, 1.0 / math.sqrt(D))
+    record("vit_multiview_fused_qkv", lambda h, a=args: fa.fa_fwd_strided(*a, h), vit_flops, vit_bytes)
+    # ViT as a packed variable-length batch of three 256-token views
+    qp, kp, vp = (torch.randn(B * S, H, D, device=device).to(torch.bfloat16) for _ in range(3))
+    outp, lsep = torch.empty_like(qp), torch.empty(H, B * S, dtype=torch.float32, device=device)
+    cu = torch.tensor([0, S, 2 * S, 3 * S], dtype=torch.int32, device=device)
+    args = (qp.data_ptr(), kp.data_ptr(), vp.data_ptr(), outp.data_ptr(), lsep.data_ptr(), cu.data_ptr(),
+            cu.data_ptr(), B, S, S, B * S, B * S, H, H, D, fa.FA_BF16, 0, 1.0 / math.sqrt(D))
+    record("vit_multiview_varlen", lambda h, a=args: fa.fa_fwd_varlen(*a, h), vit_flops, vit_bytes)
+    # causal chunk: 64 new positions (8 query heads, 1 K/V head, D256) attending a 1024-key cache
+    Sq, Sk, Hq, Dd = 64, 1024, 8, 256
+    q, k, v, _ = make_custom(1, Sq, Sk, Hq, 1, Dd, seed=3)
+    q, k, v = (t.to(device) for t in (q, k, v))
+    out, lse = torch.empty_like(q), torch.empty(1, Hq, Sq, dtype=torch.float32, device=device)
+    fa.ensure_workspace(q.device, fa.fa_fwd_workspace_bytes(1, Sq, Sk, Hq, 1, Dd, 1))
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), 1, Sq, Sk, Hq, 1, Dd, 1, 0,
+            0.0625)
+    record("causal_chunk_64x1024_gqa", lambda h, a=args: fa.fa_fwd(*a, h), 4 * Dd * pairs_causal(Sq, Sk, Hq),
+           (2 * Sq * Hq + 2 * Sk) * Dd * 2 + Hq * Sq * 4)
+    # causal decode: one new position over the padded 1056-key prefix cache (1009 valid keys)
+    Sq, Sk, n = 1, 1056, 1009
+    q, k, v, sq = make_custom(1, Sq, Sk, Hq, 1, Dd, seed=4, n_valid=n)
+    q, k, v, sq = (t.to(device) for t in (q, k, v, sq))
+    out, lse = torch.empty_like(q), torch.empty(1, Hq, Sq, dtype=torch.float32, device=device)
+    fa.ensure_workspace(q.device, fa.fa_fwd_workspace_bytes(1, Sq, Sk, Hq, 1, Dd, 1))
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), 1, Sq, Sk, Hq, 1, Dd, 1,
+            sq.data_ptr(), 0.0625)
+    record("causal_decode_1x1009_gqa", lambda h, a=args: fa.fa_fwd(*a, h), 4 * Dd * Hq * n,
+           (2 * Sq * Hq + 2 * n) * Dd * 2 + Hq * Sq * 4)
+    return rows
+
+
 def measure(w, steps, warmup, device):
     r = Runner(w, device)
     wall, ev = time_graph(r.step, steps, warmup, device)
@@ -415,6 +483,7 @@ def main(argv=None):
             if bnd == "hbm" and name != "single_head":
                 table[name]["cold"] = cold_timing(wx, device)
         line["all_workloads"] = table
+        line["extensions"] = extension_rows(device)
     line["clocks"] = clocks()
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, budget_s=a.cpu_budget)
