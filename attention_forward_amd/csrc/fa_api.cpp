@@ -200,7 +200,7 @@ int check_strided(const void* q, const void* k, const void* v, void* out, float*
   if ((long long)B * Hkv > 65535 || (long long)Sq * (Hq / Hkv) > INT32_MAX / 2) return FA_ERR_SHAPE;
   const View* views[4] = {&vq, &vk, &vv, &vo};
   for (const View* w : views)
-    if (w->sb < 0 || w->ss < 0 || w->sh < 0) return FA_ERR_SHAPE;
+    if (w->sb < 0 || w->ss < 0 || w->sh < 0 || w->ss >= (1ll << 31) || w->sh >= (1ll << 31)) return FA_ERR_SHAPE;
   // 32-bit offsets inside the kernels: keys of one (batch, kv head) and the
   // query rows of one batch entry.
   if ((long long)Sk * vk.ss * 2 >= (1ll << 31) || (long long)Sk * vv.ss * 2 >= (1ll << 31)) return FA_ERR_SHAPE;
@@ -276,18 +276,22 @@ int run(const Plan& pl, const void* q, const void* k, const void* v, void* out, 
   p.Mp = pl.Mp;
   p.coff = Sk - Sq;
   p.lse_hs = Sq;
+  p.lse_bs = (long long)Hq * Sq;
   if (packed.cu_q != nullptr) {
     p.cu_q = packed.cu_q;
     p.cu_k = packed.cu_k;
     p.total_q = packed.total_q;
     p.total_k = packed.total_k;
     p.lse_hs = packed.total_q;
+    p.lse_bs = 0;  // a sequence's rows are located by its query offset
     // Grids are planned for the longest sequences; a sequence may pair any
     // query count with up to Sk keys, so causal blocks plan for all Sk keys.
     p.coff = Sk - 1;
   }
   p.kps = pl.kps;
   p.nrb = pl.nrb;
+  p.nrb_m = 0xffffffffu / (uint32_t)pl.nrb;
+  p.hkv_m = 0xffffffffu / (uint32_t)Hkv;
   p.zmax = pl.zmax;
   p.scale_log2 = scale * 1.4426950408889634f;
   p.q_sb = vq.sb, p.q_ss = vq.ss, p.q_sh = vq.sh;

@@ -352,15 +352,39 @@ __device__ __forceinline__ void pv_tile(f32x4_t (&oacc)[G::DT][QT], const uint32
 // whose (batch, kv head) count is a multiple of 8, block n is given to
 // (batch*kv head, row block) such that every row block of one (batch, kv
 // head) lands on the same XCD and its K/V is fetched into one L2 only.
-__device__ __forceinline__ void xcd_block(int& bh, int& rb) {
+// The grid sizes come from the launch parameters (nrb row blocks by B*Hkv),
+// not from the dispatch packet, which would take two more dependent scalar
+// loads before the first tile copy.
+// n / d for 0 <= n < 2^31 and d >= 1, given m = floor((2^32 - 1) / d): the
+// high half of n*m is the quotient or one less (m > (2^32 - 1) / d - 1 and
+// n < 2^31 keep the error of n*m / 2^32 below one), so one correction step
+// makes it exact.  Scalar multiplies only, where the compiler's division
+// would go through a vector reciprocal and back.
+__device__ __forceinline__ int udiv(int n, int d, uint32_t m) {
+  const uint32_t q = __umulhi((uint32_t)n, m);
+  return (int)(q + ((uint32_t)n - q * (uint32_t)d >= (uint32_t)d ? 1u : 0u));
+}
+
+__device__ __forceinline__ void xcd_block(const FwdParams& p, int& bh, int& rb) {
   bh = blockIdx.y;
   rb = blockIdx.x;
-  if (gridDim.z == 1 && (gridDim.y & 7) == 0) {
-    const int n = blockIdx.x + gridDim.x * blockIdx.y;  // dispatch order
-    const int slot = n >> 3, grp = slot / gridDim.x;
+  const int nbh = p.B * p.Hkv;
+  if ((nbh & 7) == 0) {
+    const int n = blockIdx.x + p.nrb * blockIdx.y;  // dispatch order
+    const int slot = n >> 3, grp = udiv(slot, p.nrb, p.nrb_m);
     bh = (n & 7) + 8 * grp;
-    rb = slot - grp * gridDim.x;
+    rb = slot - grp * p.nrb;
   }
+}
+
+// Loads the launch parameters the prologue needs at kernel entry, together:
+// the compiler would otherwise fetch the strides only after the first
+// branch, one more scalar-memory round trip before the first tile copy.
+__device__ __forceinline__ void pin_params(const FwdParams& p) {
+  asm volatile("" ::"s"(p.q_sb), "s"(p.q_ss), "s"(p.q_sh), "s"(p.k_sb), "s"(p.k_ss), "s"(p.k_sh), "s"(p.v_sb),
+               "s"(p.v_ss), "s"(p.v_sh), "s"(p.o_ss), "s"(p.o_sh), "s"(p.o_sb));
+  asm volatile("" ::"s"(p.nrb), "s"(p.nrb_m), "s"(p.hkv_m), "s"(p.kps), "s"(p.coff), "s"(p.zmax), "s"(p.Mp),
+               "s"(p.lse_hs), "s"(p.lse_bs), "s"(p.total_q), "s"(p.total_k));
 }
 
 // ---- straight-line tile phases for the software-pipelined loop
@@ -504,6 +528,15 @@ __host__ __device__ __forceinline__ int causal_kmax(int rb, int rows, int Mp, in
   return k < 0 ? 0 : (k > Sk ? Sk : k);
 }
 
+// Element offset b*sb + r*ss + h*sh of a (batch, position, head) view.
+// Indices and strides are non-negative and the host keeps the position and
+// head strides below 2^31, so those two terms are 32x32-bit products; only
+// the batch term takes a 64-bit stride.
+__device__ __forceinline__ uint64_t view_off(int b, int r, int h, long long sb, long long ss, long long sh) {
+  return (uint64_t)(uint32_t)b * (uint64_t)sb + (uint64_t)(uint32_t)r * (uint32_t)ss +
+         (uint64_t)(uint32_t)h * (uint32_t)sh;
+}
+
 // Rows and keys of batch entry b.  Fixed shape: query positions 0..Sq-1
 // and keys 0..n-1, n from seqused_k.  Packed variable-length batch: the
 // b-th sequence, its offsets read on the device and clamped into the
@@ -517,7 +550,13 @@ struct Seq {
 
 __device__ __forceinline__ Seq seq_of(const FwdParams& p, int b) {
   Seq r;
-  if (p.cu_q != nullptr) {
+  r.q0 = 0;
+  r.sq = p.Sq;
+  r.k0 = 0;
+  r.nk = p.Sk;
+  // The fixed-shape path falls straight through: a taken branch this early
+  // costs an instruction-cache miss before the first tile copy is issued.
+  if (__builtin_expect(p.cu_q != nullptr, 0)) {
     int a = min(max(p.cu_q[b], 0), p.total_q), e = min(max(p.cu_q[b + 1], a), p.total_q);
     r.q0 = a;
     r.sq = min(e - a, p.Sq);
@@ -525,18 +564,15 @@ __device__ __forceinline__ Seq seq_of(const FwdParams& p, int b) {
     e = min(max(p.cu_k[b + 1], a), p.total_k);
     r.k0 = a;
     r.nk = min(e - a, p.Sk);
-  } else {
-    r.q0 = 0;
-    r.sq = p.Sq;
-    r.k0 = 0;
-    r.nk = p.seqused != nullptr ? min(max(p.seqused[b], 0), p.Sk) : p.Sk;
+  } else if (p.seqused != nullptr) {
+    r.nk = min(max(p.seqused[b], 0), p.Sk);
   }
   // uniform per workgroup: keeps buffer resources and loop bounds scalar
   r.q0 = __builtin_amdgcn_readfirstlane(r.q0);
   r.sq = __builtin_amdgcn_readfirstlane(r.sq);
   r.k0 = __builtin_amdgcn_readfirstlane(r.k0);
   r.nk = __builtin_amdgcn_readfirstlane(r.nk);
-  r.lse0 = p.cu_q != nullptr ? (long long)r.q0 : (long long)b * p.Hq * p.Sq;
+  r.lse0 = (long long)b * p.lse_bs + r.q0;  // one of the two terms is zero
   return r;
 }
 
@@ -558,14 +594,15 @@ fwd_kernel(const FwdParams p) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: wave-level addresses stay scalar
   const int col = lane & 15, grp = lane >> 4;
+  pin_params(p);
   int bh, rb_x;
-  if constexpr (CAUSAL) {
+  if constexpr (CAUSAL || SPLIT) {
     bh = blockIdx.y;
     rb_x = blockIdx.x;
   } else {
-    xcd_block(bh, rb_x);
+    xcd_block(p, bh, rb_x);
   }
-  const int b = bh / p.Hkv, hk = bh - b * p.Hkv;
+  const int b = udiv(bh, p.Hkv, p.hkv_m), hk = bh - b * p.Hkv;
   const int g = p.g;
 
   const Seq sq = seq_of(p, b);
@@ -627,8 +664,8 @@ fwd_kernel(const FwdParams p) {
   // ---- K/V tile copies.  Buffers start at this (batch, kv head)'s first key
   // and end after key kend - 1, so every key at or past kend reads as zero.
   const uint32_t rstride_k = (uint32_t)(p.k_ss * 2), rstride_v = (uint32_t)(p.v_ss * 2);  // bytes between keys
-  const u32x4_t rk = make_rsrc(p.k + b * p.k_sb + sq.k0 * p.k_ss + hk * p.k_sh, (uint32_t)kend * rstride_k);
-  const u32x4_t rv = make_rsrc(p.v + b * p.v_sb + sq.k0 * p.v_ss + hk * p.v_sh, (uint32_t)kend * rstride_v);
+  const u32x4_t rk = make_rsrc(p.k + view_off(b, sq.k0, hk, p.k_sb, p.k_ss, p.k_sh), (uint32_t)kend * rstride_k);
+  const u32x4_t rv = make_rsrc(p.v + view_off(b, sq.k0, hk, p.v_sb, p.v_ss, p.v_sh), (uint32_t)kend * rstride_v);
   // Per-thread source offsets of its slots within a tile: slot P holds row
   // P / (STR/16), chunk P % (STR/16); padding chunks and trash windows read
   // out of range (zeros, no memory access).
@@ -704,7 +741,7 @@ fwd_kernel(const FwdParams p) {
     const int s = ok ? r / g : 0;
     const int hh = ok ? r - s * g : 0;
     srow[t] = ok ? s + doff : -1;  // causal: the row's diagonal key
-    const uint16_t* qp = p.q + b * p.q_sb + (sq.q0 + s) * p.q_ss + (hk * g + hh) * p.q_sh;
+    const uint16_t* qp = p.q + view_off(b, sq.q0 + s, hk * g + hh, p.q_sb, p.q_ss, p.q_sh);
 #pragma unroll
     for (int c = 0; c < G::KC; ++c) {
       const int d0 = 32 * c + 8 * grp;
@@ -789,7 +826,7 @@ fwd_kernel(const FwdParams p) {
       const int s = r / g, hh = r - s * g;
       const float l = l_tot[t];
       const float inv = (l > 0.f) ? 1.0f / l : 0.f;
-      uint16_t* op = p.out + b * p.o_sb + (sq.q0 + s) * p.o_ss + (hk * g + hh) * p.o_sh;
+      uint16_t* op = p.out + view_off(b, sq.q0 + s, hk * g + hh, p.o_sb, p.o_ss, p.o_sh);
 #pragma unroll
       for (int dt = 0; dt < G::DT; ++dt) {
         const int d = 16 * dt + 4 * grp;
@@ -843,6 +880,7 @@ __global__ void __launch_bounds__(KW * 64, 1)
 fwd_ks_kernel(const FwdParams p) {
   using G = Geo<D, QT, 1, BN, DTY>;  // per-wave geometry: one wave issues its own tile copies
   constexpr int ROWS = 16 * QT;
+  pin_params(p);
   static_assert(!G::TRASH, "per-wave tiles must be whole 64-slot windows");
   // LDS: KW per-wave K/V buffers, then the workgroup's Q tile (rows at the K
   // stride, read like K fragments); after the main loop the same memory is
@@ -861,7 +899,7 @@ fwd_ks_kernel(const FwdParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: wave-level addresses stay scalar
   const int col = lane & 15, grp = lane >> 4;
   const int bh = blockIdx.y;
-  const int b = bh / p.Hkv, hk = bh - b * p.Hkv;
+  const int b = udiv(bh, p.Hkv, p.hkv_m), hk = bh - b * p.Hkv;
   const int g = p.g;
 
   const Seq sq = seq_of(p, b);
@@ -914,8 +952,8 @@ fwd_ks_kernel(const FwdParams p) {
 
   // ---- this wave's K/V copies (see fwd_kernel: out-of-range keys read as 0)
   const uint32_t rstride_k = (uint32_t)(p.k_ss * 2), rstride_v = (uint32_t)(p.v_ss * 2);
-  const u32x4_t rk = make_rsrc(p.k + b * p.k_sb + sq.k0 * p.k_ss + hk * p.k_sh, (uint32_t)kend * rstride_k);
-  const u32x4_t rv = make_rsrc(p.v + b * p.v_sb + sq.k0 * p.v_ss + hk * p.v_sh, (uint32_t)kend * rstride_v);
+  const u32x4_t rk = make_rsrc(p.k + view_off(b, sq.k0, hk, p.k_sb, p.k_ss, p.k_sh), (uint32_t)kend * rstride_k);
+  const u32x4_t rv = make_rsrc(p.v + view_off(b, sq.k0, hk, p.v_sb, p.v_ss, p.v_sh), (uint32_t)kend * rstride_v);
   uint32_t voff_k[G::LPT_K], voff_v[G::LPT_V];
 #pragma unroll
   for (int j = 0; j < G::LPT_K; ++j) {
@@ -960,7 +998,7 @@ fwd_ks_kernel(const FwdParams p) {
     const int s_first = row0 / g;
     const int s_last = (min(row0 + ROWS, Mp) - 1) / g;
     const uint32_t qrow_b = (uint32_t)(p.q_ss * 2), qhead_b = (uint32_t)(p.q_sh * 2);
-    const u32x4_t rq = make_rsrc(p.q + b * p.q_sb + (sq.q0 + s_first) * p.q_ss + hk * g * p.q_sh,
+    const u32x4_t rq = make_rsrc(p.q + view_off(b, sq.q0 + s_first, hk * g, p.q_sb, p.q_ss, p.q_sh),
                                  (uint32_t)(s_last - s_first) * qrow_b + (uint32_t)(g - 1) * qhead_b + D * 2);
     const uint32_t lds_q = (uint32_t)(uintptr_t)(lds_void_t*)(smem + Q_OFF);
     for (int j = wave; j < Q_INSTR; j += KW) {
@@ -1081,7 +1119,7 @@ fwd_ks_kernel(const FwdParams p) {
         if constexpr (!SPLIT) {
           const u32x4_t o = {G::E::pack(a0[0], a0[1]), G::E::pack(a0[2], a0[3]), G::E::pack(a1[0], a1[1]),
                              G::E::pack(a1[2], a1[3])};
-          *reinterpret_cast<u32x4_t*>(p.out + b * p.o_sb + (sq.q0 + s) * p.o_ss + (hk * g + hh) * p.o_sh + 8 * ch) = o;
+          *reinterpret_cast<u32x4_t*>(p.out + view_off(b, sq.q0 + s, hk * g + hh, p.o_sb, p.o_ss, p.o_sh) + 8 * ch) = o;
         } else {
           const size_t prow = (((size_t)bh * p.nrb + blk.rb) * p.zmax + blk.z) * ROWS + rl;
           float* po = p.ws_o + prow * D + 8 * ch;
@@ -1122,7 +1160,7 @@ combine_kernel(const FwdParams p) {
   const int ch = rem % CPR;
   const int r = rb * ROWS_WG + rl;
   const int g = p.g;
-  const int b = bh / p.Hkv, hk = bh - b * p.Hkv;
+  const int b = udiv(bh, p.Hkv, p.hkv_m), hk = bh - b * p.Hkv;
   const Seq sq = seq_of(p, b);
   if (r >= sq.sq * g) return;  // past the end of this batch entry's queries
   int nz = p.zmax;
@@ -1163,7 +1201,7 @@ combine_kernel(const FwdParams p) {
   const float inv = (L > 0.f) ? 1.0f / L : 0.f;
   const u32x4_t o = {E::pack(a0[0] * inv, a0[1] * inv), E::pack(a0[2] * inv, a0[3] * inv),
                      E::pack(a1[0] * inv, a1[1] * inv), E::pack(a1[2] * inv, a1[3] * inv)};
-  *reinterpret_cast<u32x4_t*>(p.out + b * p.o_sb + (sq.q0 + s) * p.o_ss + (hk * g + hh) * p.o_sh + 8 * ch) = o;
+  *reinterpret_cast<u32x4_t*>(p.out + view_off(b, sq.q0 + s, hk * g + hh, p.o_sb, p.o_ss, p.o_sh) + 8 * ch) = o;
   if (ch == 0 && p.lse != nullptr) {
     const float lse = (L > 0.f) ? (M + __log2f(L)) * kLn2 : -INFINITY;
     p.lse[sq.lse0 + (long long)(hk * g + hh) * p.lse_hs + s] = lse;

@@ -22,6 +22,7 @@ struct FwdParams {
   const int32_t* cu_k;
   int total_q, total_k;    // token rows of q / out and of k / v (packed batch)
   long long lse_hs;        // lse elements between heads: Sq, or total_q for a packed batch
+  long long lse_bs;        // lse elements between batch entries: Hq * Sq, or 0 for a packed batch
   // Split-KV workspace (split variants only).  Partial rows are indexed
   // ((bh * nrb + row_block) * zmax + split) * rows_per_block + row_in_block.
   float* ws_o;             // partial O / l, fp32, D per partial row
@@ -32,6 +33,7 @@ struct FwdParams {
   int coff;                // Sk - Sq: causal diagonal offset of the full key buffer (grid planning)
   int kps;                 // keys per split (multiple of the key tile), split variants only
   int nrb;                 // row blocks per (batch, kv head)
+  uint32_t nrb_m, hkv_m;   // floor((2^32 - 1) / nrb) and floor((2^32 - 1) / Hkv), multipliers for udiv
   int zmax;                // most splits of any row block
   float scale_log2;        // scale * log2(e)
   // Element strides of the views (batch, sequence, head); head_dim is

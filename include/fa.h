@@ -122,7 +122,8 @@ enum {
  *   the one fa_fwd_plan reports.  With contiguous strides
  *   (S*H*D, H*D, D) and FA_BF16 it computes exactly what fa_fwd does.
  * Extra requirements: strides >= 0 and multiples of 8 elements (16-byte
- * rows, FA_ERR_ALIGN otherwise); key rows of one head do not overlap
+ * rows, FA_ERR_ALIGN otherwise); sequence and head strides below 2^31
+ * elements (FA_ERR_SHAPE); key rows of one head do not overlap
  * (k_ss, v_ss >= D when Sk > 1) and no two output rows overlap
  * (FA_ERR_SHAPE); Sk*k_ss*2 and Sk*v_ss*2 bytes, and the bytes from a
  * batch entry's first query row to its last, below 2^31 (FA_ERR_SHAPE);

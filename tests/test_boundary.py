@@ -125,6 +125,10 @@ def _call_strided(qs=None, ks=None, vs=None, os_=None, dtype=fa.FA_BF16, **over)
     (dict(os_=(64 * 8 * 256, 8 * 256, 128)), fa.FA_ERR_SHAPE),
     # 32-bit key offsets of one (batch, kv head)
     (dict(ks=(0, 1 << 24, 256)), fa.FA_ERR_SHAPE),
+    # head strides below 2^31 elements (32x32-bit index products); with one
+    # kv head nothing else about these views is wrong
+    (dict(ks=(64 * 256, 256, 1 << 31)), fa.FA_ERR_SHAPE),
+    (dict(vs=(64 * 256, 256, 1 << 32)), fa.FA_ERR_SHAPE),
     # out inside the span of a strided q (one buffer)
     (dict(out=Q + 512, os_=(64 * 8 * 3 * 256, 8 * 3 * 256, 256), qs=(64 * 8 * 3 * 256, 8 * 3 * 256, 256)),
      fa.FA_ERR_ALIAS),
