@@ -51,9 +51,10 @@ struct Plan {
   size_t ws_o_bytes = 0, ws_ml_bytes = 0, ws_bytes = 0;
 };
 
-// Packed rows one workgroup covers: its waves own different rows (kw == 1)
-// or all share the same 16*qt rows and split the keys (kw > 1).
-int rows_per_block(const fa::LaunchPlan& l) { return (l.kw > 1 ? 1 : l.nw) * 16 * l.qt; }
+// Packed rows one workgroup covers: nw / kw waves on different rows, each
+// row set shared by kw waves that split the keys (kw == 1: every wave has
+// its own rows; kw == nw: all waves on the same 16*qt rows).
+int rows_per_block(const fa::LaunchPlan& l) { return (l.nw / l.kw) * 16 * l.qt; }
 
 // Fills in the derived fields (row blocks, split count, workspace layout) of
 // a plan whose variant and keys-per-split are set.  kps == 0: no split.

@@ -582,17 +582,25 @@ struct RowBlock {
   int kbeg, kend;
 };
 
-template <int D, int QT, int NW, int BN, int NST, bool CAUSAL, bool SPLIT, int DTY>
-__global__ void __launch_bounds__(NW * 64, 1)
+template <int D, int QT, int NW, int BN, int NST, int KG, bool CAUSAL, bool SPLIT, int DTY>
+__global__ void __launch_bounds__(NW * KG * 64, 1)
 fwd_kernel(const FwdParams p) {
-  using G = Geo<D, QT, NW, BN, DTY>;
+  using G = Geo<D, QT, NW, BN, DTY>;  // geometry of one key group: NW waves on different rows
   static_assert(NST >= 2, "at least double buffering");
-  __shared__ __attribute__((aligned(16))) uint8_t stage[NST * G::STAGE_B];
-  __shared__ __attribute__((aligned(16))) uint8_t trash[G::TRASH ? NW * 1024 : 16];
+  static_assert(KG == 1 || (KG == 2 && NST == 2), "two key groups run the two-stage loop");
+  static_assert(KG * NST * G::STAGE_B + (G::TRASH ? NW * KG * 1024 : 16) <= 160 * 1024, "LDS of one workgroup");
+  __shared__ __attribute__((aligned(16))) uint8_t stage[KG * NST * G::STAGE_B];
+  __shared__ __attribute__((aligned(16))) uint8_t trash[G::TRASH ? NW * KG * 1024 : 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: wave-level addresses stay scalar
+  // KG key groups of NW waves: group kg takes key tiles kg, kg+KG, ... of the
+  // block's range through its own stage ring, wave w of each group owns the
+  // same rows, and the groups' partial results are merged at the end.
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: wave-level addresses stay scalar
+  const int kg = KG > 1 ? wid / NW : 0;
+  const int wave = wid - kg * NW;                            // row wave within the group
+  const int gtid = tid - kg * NW * 64;                       // thread within the group
   const int col = lane & 15, grp = lane >> 4;
   pin_params(p);
   int bh, rb_x;
@@ -672,25 +680,27 @@ fwd_kernel(const FwdParams p) {
   uint32_t voff_k[G::LPT_K], voff_v[G::LPT_V];
 #pragma unroll
   for (int j = 0; j < G::LPT_K; ++j) {
-    const int P = j * G::NT + tid;
+    const int P = j * G::NT + gtid;
     const int row = P / (G::KSTR / 16), ch = P - row * (G::KSTR / 16);
     voff_k[j] = (P < G::K_SLOTS && ch < G::CPR) ? row * rstride_k + ch * 16 : kOutOfRange;
   }
 #pragma unroll
   for (int j = 0; j < G::LPT_V; ++j) {
-    const int P = j * G::NT + tid;
+    const int P = j * G::NT + gtid;
     const int row = P / (G::VSTR / 16), ch = P - row * (G::VSTR / 16);
     voff_v[j] = (P < G::V_SLOTS && ch < G::CPR) ? row * rstride_v + ch * 16 : kOutOfRange;
   }
-  const uint32_t lds_stage0 = (uint32_t)(uintptr_t)(lds_void_t*)stage;
-  const uint32_t lds_trash = (uint32_t)(uintptr_t)(lds_void_t*)trash + wave * 1024;
+  uint8_t* const gstage = stage + kg * NST * G::STAGE_B;  // this group's stage ring
+  const uint32_t lds_stage0 = (uint32_t)(uintptr_t)(lds_void_t*)gstage;
+  const uint32_t lds_trash = (uint32_t)(uintptr_t)(lds_void_t*)trash + wid * 1024;
   // The tile's key offset goes into the per-lane offset (not soffset), so
   // the range check sees the full offset; key bytes per batch and head stay
   // below 2^31 (checked on the host), so adding it to kOutOfRange cannot wrap.
+  // Group-local tile j holds keys kbeg + (kg + j*KG)*BN ...; it sits in stage j % NST.
   auto issue = [&](int it) __attribute__((always_inline)) {
     const uint32_t st = lds_stage0 + (it % NST) * G::STAGE_B;
-    const uint32_t toff_k = (uint32_t)(kbeg + it * BN) * rstride_k;
-    const uint32_t toff_v = (uint32_t)(kbeg + it * BN) * rstride_v;
+    const uint32_t toff_k = (uint32_t)(kbeg + (kg + it * KG) * BN) * rstride_k;
+    const uint32_t toff_v = (uint32_t)(kbeg + (kg + it * KG) * BN) * rstride_v;
 #pragma unroll
     for (int j = 0; j < G::LPT_K; ++j) {
       const int pbase = j * G::NT + wave * 64;
@@ -726,7 +736,9 @@ fwd_kernel(const FwdParams p) {
   // and the loads of tiles it+1 .. it+NST-1 are in flight while tile it is
   // computed.  Each tile costs every thread exactly LPT copies, so waiting
   // until at most (NST-2)*LPT copies are outstanding means tile it landed.
-  const int ntiles = kend > kbeg ? (kend - kbeg + BN - 1) / BN : 0;
+  const int ntiles_all = kend > kbeg ? (kend - kbeg + BN - 1) / BN : 0;
+  const int ntiles = ntiles_all > kg ? (ntiles_all - kg + KG - 1) / KG : 0;  // this group's tiles
+  const int nsteps = (ntiles_all + KG - 1) / KG;                             // loop trips of every group
 #pragma unroll
   for (int it = 0; it < NST - 1; ++it)
     if (it < ntiles) issue(it);
@@ -755,15 +767,13 @@ fwd_kernel(const FwdParams p) {
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 
   if constexpr (NST == 2) {
-    constexpr int kAhead = (NST - 2) * G::LPT;  // copies allowed in flight after tile it
-    for (int it = 0; it < ntiles; ++it) {
-      if (it + NST - 2 < ntiles)
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(kAhead));  // tile it landed (this thread's copies)
-      else
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));       // near the end: everything landed
-      __syncthreads();                                   // everyone's copies; stage (it-1) % NST is free
-      if (it + NST - 1 < ntiles) issue(it + NST - 1);
-      compute_tile(stage + (it % NST) * G::STAGE_B, kbeg + it * BN);
+    // Every group makes the same number of trips (the workgroup barrier is
+    // shared); a group past its last tile only waits.
+    for (int it = 0; it < nsteps; ++it) {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // tile it landed (this thread's copies)
+      __syncthreads();                            // everyone's copies; the other stage is free
+      if (it + 1 < ntiles) issue(it + 1);
+      if (it < ntiles) compute_tile(gstage + (it & 1) * G::STAGE_B, kbeg + (kg + it * KG) * BN);
     }
   } else {
     // Software-pipelined loop (three or more stages).  Iteration it issues the
@@ -816,6 +826,43 @@ fwd_kernel(const FwdParams p) {
   float l_tot[QT];
 #pragma unroll
   for (int t = 0; t < QT; ++t) l_tot[t] = group_sum(l_run[t]);
+
+  if constexpr (KG > 1) {
+    // ---- merge of the two key groups through LDS: wave w of group 1 stores
+    // its O (not yet divided by l) and (m, l) per row; the same lane of wave w
+    // of group 0 holds the same elements of the same rows and combines them:
+    // M = max of the non-empty m, O = O0 2^(m0-M) + O1 2^(m1-M), l likewise.
+    constexpr int OSTR = G::DT * 64 + 16;  // bytes per merged row (padded)
+    static_assert(G::ROWS_WG * (OSTR + 8) <= KG * NST * G::STAGE_B, "merge area inside the stages");
+    float* mls = reinterpret_cast<float*>(stage + G::ROWS_WG * OSTR);  // [row] (m, l)
+    __syncthreads();  // every wave is done with its stages: the LDS becomes the merge area
+    if (kg == 1) {
+#pragma unroll
+      for (int t = 0; t < QT; ++t) {
+        const int rr = wave * 16 * QT + 16 * t + col;
+#pragma unroll
+        for (int dt = 0; dt < G::DT; ++dt)
+          *reinterpret_cast<f32x4_t*>(stage + rr * OSTR + (16 * dt + 4 * grp) * 4) = oacc[dt][t];
+        if (grp == 0) *reinterpret_cast<u32x2_t*>(mls + 2 * rr) = u32x2_t{__float_as_uint(m_run[t]), __float_as_uint(l_tot[t])};
+      }
+    }
+    __syncthreads();
+    if (kg == 1) return;
+#pragma unroll
+    for (int t = 0; t < QT; ++t) {
+      const int rr = wave * 16 * QT + 16 * t + col;
+      const float m1 = mls[2 * rr], l1 = mls[2 * rr + 1];
+      const float m0 = m_run[t], l0 = l_tot[t];
+      const float M = fmaxf(l0 > 0.f ? m0 : -INFINITY, l1 > 0.f ? m1 : -INFINITY);
+      const float a0 = l0 > 0.f ? __builtin_amdgcn_exp2f(m0 - M) : 0.f;
+      const float a1 = l1 > 0.f ? __builtin_amdgcn_exp2f(m1 - M) : 0.f;
+      m_run[t] = M;
+      l_tot[t] = l0 * a0 + l1 * a1;
+#pragma unroll
+      for (int dt = 0; dt < G::DT; ++dt)
+        oacc[dt][t] = oacc[dt][t] * a0 + *reinterpret_cast<const f32x4_t*>(stage + rr * OSTR + (16 * dt + 4 * grp) * 4) * a1;
+    }
+  }
 
   if (!wave_active) return;
   if constexpr (!SPLIT) {
@@ -1210,7 +1257,7 @@ combine_kernel(const FwdParams p) {
 
 // ------------------------------------------------------------------ launch
 
-template <int D, int QT, int NW, int BN, int NST, bool CAUSAL, bool SPLIT, int DTY>
+template <int D, int QT, int NW, int BN, int NST, int KG, bool CAUSAL, bool SPLIT, int DTY>
 static hipError_t launch_variant(const FwdParams& p, const LaunchPlan& plan, hipStream_t stream) {
   using G = Geo<D, QT, NW, BN, DTY>;
   const int nrb = (p.Mp + G::ROWS_WG - 1) / G::ROWS_WG;
@@ -1224,7 +1271,7 @@ static hipError_t launch_variant(const FwdParams& p, const LaunchPlan& plan, hip
   } else {
     grid = dim3(nrb, p.B * p.Hkv, SPLIT ? plan.nsplit : 1);
   }
-  hipLaunchKernelGGL((fwd_kernel<D, QT, NW, BN, NST, CAUSAL, SPLIT, DTY>), grid, dim3(NW * 64), 0, stream, p);
+  hipLaunchKernelGGL((fwd_kernel<D, QT, NW, BN, NST, KG, CAUSAL, SPLIT, DTY>), grid, dim3(NW * KG * 64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !SPLIT) return e;
   const long long threads = (long long)p.B * p.Hkv * nrb * G::ROWS_WG * (D / 8);
@@ -1257,31 +1304,37 @@ static hipError_t launch_ks_variant(const FwdParams& p, const LaunchPlan& plan, 
 }
 
 // The compiled variants.  Row-split (fwd_kernel) entries: element type, head
-// dim, rows per wave / 16, waves, keys per tile, K/V stages in LDS (two: one
-// tile computed while the next loads; three or more: the software-pipelined
-// loop).  Key-split (fwd_ks_kernel) entries: element type, head dim, rows per
-// wave / 16, waves (all on the same rows), keys per tile.  Every variant is
-// built with and without causal masking and with and without the split-KV
-// partial output.  fp16 has the variants the default plan uses.
-#define FA_VARIANTS(X)        \
-  X(kBf16, 64, 1, 4, 64, 2)   \
-  X(kBf16, 64, 2, 2, 64, 2)   \
-  X(kBf16, 64, 2, 4, 64, 2)   \
-  X(kBf16, 64, 1, 4, 64, 3)   \
-  X(kBf16, 72, 1, 4, 64, 2)   \
-  X(kBf16, 72, 1, 4, 64, 3)   \
-  X(kBf16, 72, 1, 4, 64, 4)   \
-  X(kBf16, 72, 2, 2, 64, 2)   \
-  X(kBf16, 72, 2, 2, 64, 3)   \
-  X(kBf16, 72, 2, 4, 64, 2)   \
-  X(kBf16, 256, 1, 4, 32, 2)  \
-  X(kBf16, 256, 1, 4, 32, 4)  \
-  X(kBf16, 256, 1, 4, 64, 2)  \
-  X(kBf16, 256, 2, 4, 32, 2)  \
-  X(kBf16, 256, 2, 4, 32, 4)  \
-  X(kBf16, 256, 2, 4, 64, 2)  \
-  X(kF16, 64, 1, 4, 64, 2)    \
-  X(kF16, 72, 1, 4, 64, 2)
+// dim, rows per wave / 16, waves per key group, key groups, keys per tile,
+// K/V stages in LDS (two: one tile computed while the next loads; three or
+// more: the software-pipelined loop).  With two key groups the workgroup
+// has twice the waves on the same rows, each group taking every other key
+// tile, and the two partials are merged in LDS.  Key-split (fwd_ks_kernel)
+// entries: element type, head dim, rows per wave / 16, waves (all on the
+// same rows), keys per tile.  Every variant is built with and without causal
+// masking and with and without the split-KV partial output.  fp16 has the
+// variants the default plan uses.
+#define FA_VARIANTS(X)           \
+  X(kBf16, 64, 1, 4, 1, 64, 2)   \
+  X(kBf16, 64, 2, 2, 1, 64, 2)   \
+  X(kBf16, 64, 2, 4, 1, 64, 2)   \
+  X(kBf16, 64, 1, 4, 1, 64, 3)   \
+  X(kBf16, 64, 1, 4, 2, 64, 2)   \
+  X(kBf16, 72, 1, 4, 1, 64, 2)   \
+  X(kBf16, 72, 1, 4, 1, 64, 3)   \
+  X(kBf16, 72, 1, 4, 1, 64, 4)   \
+  X(kBf16, 72, 2, 2, 1, 64, 2)   \
+  X(kBf16, 72, 2, 2, 1, 64, 3)   \
+  X(kBf16, 72, 2, 4, 1, 64, 2)   \
+  X(kBf16, 72, 1, 4, 2, 64, 2)   \
+  X(kBf16, 72, 1, 2, 2, 64, 2)   \
+  X(kBf16, 256, 1, 4, 1, 32, 2)  \
+  X(kBf16, 256, 1, 4, 1, 32, 4)  \
+  X(kBf16, 256, 1, 4, 1, 64, 2)  \
+  X(kBf16, 256, 2, 4, 1, 32, 2)  \
+  X(kBf16, 256, 2, 4, 1, 32, 4)  \
+  X(kBf16, 256, 2, 4, 1, 64, 2)  \
+  X(kF16, 64, 1, 4, 1, 64, 2)    \
+  X(kF16, 72, 1, 4, 1, 64, 2)
 
 #define FA_KS_VARIANTS(X)  \
   X(kBf16, 64, 2, 4, 64)   \
@@ -1290,15 +1343,20 @@ static hipError_t launch_ks_variant(const FwdParams& p, const LaunchPlan& plan, 
   X(kBf16, 256, 2, 2, 32)  \
   X(kF16, 256, 2, 4, 32)
 
+// (nw, kw) of a plan: kw == 1, waves on different rows; kw == nw, every wave
+// on the same rows (key-split kernel); otherwise kw key groups of nw / kw
+// waves each (row-split kernel).
 bool variant_exists(int D, int qt, int nw, int kw, int bn, int nst, int dtype) {
-  if (kw <= 1) {
-#define FA_MATCH(t_, d_, q_, n_, b_, s_) \
-  if (dtype == t_ && D == d_ && qt == q_ && nw == n_ && bn == b_ && nst == s_) return true;
+  if (kw < 1 || nw < kw || nw % kw != 0) return false;
+  if (kw == 1 || kw < nw) {
+    const int n = nw / kw;
+#define FA_MATCH(t_, d_, q_, n_, g_, b_, s_) \
+  if (dtype == t_ && D == d_ && qt == q_ && n == n_ && kw == g_ && bn == b_ && nst == s_) return true;
     FA_VARIANTS(FA_MATCH)
 #undef FA_MATCH
     return false;
   }
-  if (nw != kw || nst != 1) return false;
+  if (nst != 1) return false;
 #define FA_KS_MATCH(t_, d_, q_, k_, b_) \
   if (dtype == t_ && D == d_ && qt == q_ && kw == k_ && bn == b_) return true;
   FA_KS_VARIANTS(FA_KS_MATCH)
@@ -1307,7 +1365,7 @@ bool variant_exists(int D, int qt, int nw, int kw, int bn, int nst, int dtype) {
 }
 
 hipError_t launch_fwd(const FwdParams& p, const LaunchPlan& plan, hipStream_t stream) {
-  if (plan.kw > 1) {
+  if (plan.kw > 1 && plan.kw == plan.nw) {
 #define FA_KS_DISPATCH(t_, d_, q_, k_, b_)                                                          \
   if (plan.dtype == t_ && plan.D == d_ && plan.qt == q_ && plan.kw == k_ && plan.bn == b_) {         \
     if (plan.causal)                                                                                \
@@ -1320,13 +1378,16 @@ hipError_t launch_fwd(const FwdParams& p, const LaunchPlan& plan, hipStream_t st
 #undef FA_KS_DISPATCH
     return hipErrorInvalidValue;
   }
-#define FA_DISPATCH(t_, d_, q_, n_, b_, s_)                                                               \
-  if (plan.dtype == t_ && plan.D == d_ && plan.qt == q_ && plan.nw == n_ && plan.bn == b_ && plan.nst == s_) { \
-    if (plan.causal)                                                                                     \
-      return plan.split ? launch_variant<d_, q_, n_, b_, s_, true, true, t_>(p, plan, stream)            \
-                        : launch_variant<d_, q_, n_, b_, s_, true, false, t_>(p, plan, stream);          \
-    return plan.split ? launch_variant<d_, q_, n_, b_, s_, false, true, t_>(p, plan, stream)             \
-                      : launch_variant<d_, q_, n_, b_, s_, false, false, t_>(p, plan, stream);           \
+  if (plan.kw < 1 || plan.nw % plan.kw != 0) return hipErrorInvalidValue;
+  const int n = plan.nw / plan.kw;
+#define FA_DISPATCH(t_, d_, q_, n_, g_, b_, s_)                                                        \
+  if (plan.dtype == t_ && plan.D == d_ && plan.qt == q_ && n == n_ && plan.kw == g_ && plan.bn == b_ && \
+      plan.nst == s_) {                                                                                \
+    if (plan.causal)                                                                                   \
+      return plan.split ? launch_variant<d_, q_, n_, b_, s_, g_, true, true, t_>(p, plan, stream)      \
+                        : launch_variant<d_, q_, n_, b_, s_, g_, true, false, t_>(p, plan, stream);    \
+    return plan.split ? launch_variant<d_, q_, n_, b_, s_, g_, false, true, t_>(p, plan, stream)       \
+                      : launch_variant<d_, q_, n_, b_, s_, g_, false, false, t_>(p, plan, stream);     \
   }
   FA_VARIANTS(FA_DISPATCH)
 #undef FA_DISPATCH

@@ -191,12 +191,15 @@ int fa_set_workspace(void* dev_ptr, size_t bytes);
  * the shape alone; these name one explicitly so that every compiled variant
  * can be timed and checked:
  *   qt   rows per wavefront / 16   (1 or 2)
- *   nw   wavefronts per workgroup  (2 or 4)
+ *   nw   wavefronts per workgroup  (2, 4 or 8)
  *   kw   1: the wavefronts own different rows and share the K/V tiles;
  *        nw: all wavefronts own the same rows and split the keys between
- *        them (nst must then be 1: each wavefront streams its own tiles)
+ *        them (nst must then be 1: each wavefront streams its own tiles);
+ *        2 with nw = 4 or 8: two groups of nw/2 wavefronts on the same
+ *        rows, each group sharing its own K/V tiles and taking every other
+ *        key tile, merged at the end (nst 2)
  *   bn   keys per tile             (32 or 64)
- *   nst  K/V tile stages in LDS    (1, 2 or 4)
+ *   nst  K/V tile stages in LDS    (1, 2, 3 or 4)
  *   kps  keys per split-KV range   (0: single pass; else a multiple of bn)
  * A combination that is not compiled returns FA_ERR_UNSUPPORTED.  Other
  * arguments, checks and errors are those of fa_fwd. */

@@ -223,7 +223,11 @@ def test_variant_rejections(lib):
     assert fa.fa_fwd_variant(*args, 3, 4, 1, 64, 2, 0, 0) == fa.FA_ERR_UNSUPPORTED   # not compiled
     assert fa.fa_fwd_variant(*args, 1, 4, 1, 32, 3, 0, 0) == fa.FA_ERR_UNSUPPORTED   # no 3-stage build
     assert fa.fa_fwd_variant(*args, 2, 4, 4, 32, 2, 0, 0) == fa.FA_ERR_UNSUPPORTED   # key-split: nst 1
-    assert fa.fa_fwd_variant(*args, 2, 4, 2, 32, 1, 0, 0) == fa.FA_ERR_UNSUPPORTED   # key-split: kw == nw
+    assert fa.fa_fwd_variant(*args, 2, 4, 2, 32, 1, 0, 0) == fa.FA_ERR_UNSUPPORTED   # key groups: nst 2, not D256
+    assert fa.fa_fwd_variant(*args, 1, 8, 2, 32, 2, 0, 0) == fa.FA_ERR_UNSUPPORTED   # key groups: not D256
+    assert fa.fa_fwd_variant(*args, 1, 4, 3, 32, 2, 0, 0) == fa.FA_ERR_UNSUPPORTED   # nw not a multiple of kw
+    assert fa.fa_fwd_variant(*args, 1, 4, 0, 32, 2, 0, 0) == fa.FA_ERR_UNSUPPORTED   # kw < 1
+    assert fa.fa_fwd_variant_workspace_bytes(1, 64, 64, 8, 1, 256, 0, 1, 4, 0, 32, 2, 0) == 0
     assert fa.fa_fwd_variant(*args, 1, 4, 1, 32, 2, 48, 0) == fa.FA_ERR_UNSUPPORTED  # kps % bn
     assert fa.fa_fwd_variant(*args, 1, 4, 1, 32, 2, -32, 0) == fa.FA_ERR_UNSUPPORTED
     bad = list(args)
