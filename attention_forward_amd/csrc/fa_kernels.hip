@@ -153,8 +153,10 @@ __device__ __forceinline__ u32x4_t make_rsrc(const void* base, uint32_t bytes) {
 #pragma clang diagnostic pop
 
 constexpr int round_up(int x, int m) { return (x + m - 1) / m * m; }
-// Smallest LDS row stride >= bytes that is 32 modulo 128 (V rows).
-constexpr int v_stride(int bytes) { return (bytes % 128 == 32) ? bytes : v_stride(bytes + 16); }
+// Smallest LDS row stride >= bytes that is an odd multiple of 16 bytes, or
+// 32 modulo 128 bytes (V rows; see Geo).
+constexpr int odd16_stride(int bytes) { return (bytes % 32 == 16) ? bytes : odd16_stride(bytes + 16); }
+constexpr int mod128_stride(int bytes) { return (bytes % 128 == 32) ? bytes : mod128_stride(bytes + 16); }
 
 // Compile-time geometry of one kernel variant.
 template <int D, int QT, int NW, int BN, int DTY = kBf16>
@@ -162,14 +164,22 @@ struct Geo {
   using E = Elem<DTY>;                           // element type of q, k, v, out
   static constexpr int CPR = D / 8;              // 16-byte chunks per K/V row
   static constexpr int ROWB = D * 2;             // bytes per K/V row
-  // LDS row strides.  A K row holds the head dim rounded up to the 32-element
-  // MFMA step (the rounding is filled with zeros by the tile copies, so the
-  // last step of S^T = K Q^T needs no per-lane guard) plus 16 bytes: an odd
-  // multiple of 16 bytes, so 16 rows read at one column with 16-byte loads
-  // hit distinct banks.  V rows are 32 bytes apart modulo 128 (the transpose
-  // reads take 32 contiguous bytes from each of 4 rows).
-  static constexpr int KSTR = round_up(D, 32) * 2 + 16;
-  static constexpr int VSTR = v_stride(ROWB);
+  // LDS row strides, chosen by measurement on gfx950.  A K row holds the
+  // head dim rounded up to the 32-element MFMA step (the rounding is filled
+  // with zeros by the tile copies, so the last step of S^T = K Q^T needs no
+  // per-lane guard) plus padding; a V row is at least as long as the
+  // fragment reads of the last head-dim tile (the transpose reads take 32
+  // bytes from each of 4 rows).  In isolation, 16 rows read at one column
+  // with 16-byte loads run at the rate of contiguous reads when the K stride
+  // is 32 modulo 64 bytes (17% slower at 16 modulo 64), and the transpose
+  // reads are 10% faster when the V stride is an odd multiple of 16 bytes.
+  // In the kernels the two interact: with both, the 256-wide key-split
+  // kernel is 4% slower.  Whole-kernel timings pick 32 bytes of K padding
+  // with V rows 32 modulo 128 for head dims up to 128 (the 72-wide workload
+  // 4% faster), and 16 bytes with odd-multiple V rows above (1-2% faster).
+  static constexpr bool WIDE = D > 128;
+  static constexpr int KSTR = round_up(D, 32) * 2 + (WIDE ? 16 : 32);
+  static constexpr int VSTR = WIDE ? odd16_stride(round_up(D, 16) * 2) : mod128_stride(round_up(D, 16) * 2);
   static constexpr int NT = NW * 64;             // threads
   static constexpr int K_SLOTS = round_up(BN * (KSTR / 16), 64);  // 16-byte slots per K tile
   static constexpr int V_SLOTS = round_up(BN * (VSTR / 16), 64);
