@@ -11,9 +11,11 @@ from .fa import (  # noqa: F401
     FA_OK,
     FAError,
     attention,
+    attention_nvfp4,
     attention_varlen,
     fa_abi_version,
     fa_fwd,
+    fa_fwd_nvfp4,
     fa_fwd_plan,
     fa_fwd_strided,
     fa_fwd_variant,
@@ -31,9 +33,11 @@ __all__ = [
     "FA_OK",
     "FAError",
     "attention",
+    "attention_nvfp4",
     "attention_varlen",
     "fa_abi_version",
     "fa_fwd",
+    "fa_fwd_nvfp4",
     "fa_fwd_plan",
     "fa_fwd_strided",
     "fa_fwd_variant",

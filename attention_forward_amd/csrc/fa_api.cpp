@@ -260,8 +260,11 @@ struct Packed {
 
 int run(const Plan& pl, const void* q, const void* k, const void* v, void* out, float* lse, int B, int Sq,
         int Sk, int Hq, int Hkv, const View& vq, const View& vk, const View& vv, const View& vo,
-        const int32_t* seqused_k, float scale, hipStream_t stream, const Packed& packed = Packed()) {
+        const int32_t* seqused_k, float scale, hipStream_t stream, const Packed& packed = Packed(),
+        void* fp4_out = nullptr, void* fp4_sf = nullptr) {
   fa::FwdParams p{};
+  p.fp4_out = static_cast<uint8_t*>(fp4_out);
+  p.fp4_sf = static_cast<uint8_t*>(fp4_sf);
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k);
   p.v = static_cast<const uint16_t*>(v);
@@ -424,6 +427,36 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* out, float*
   const View vq{0, (long long)Hq * D, D}, vk{0, (long long)Hkv * D, D};
   return run(pl, q, k, v, out, lse, B, max_seqlen_q, max_seqlen_k, Hq, Hkv, vq, vk, vk, vq, nullptr, scale, stream,
              packed);
+}
+
+int fa_fwd_nvfp4(const void* q, const void* k, const void* v, void* out_fp4, void* out_sf, float* lse, int B,
+                 int Sq, int Sk, int Hq, int Hkv, int D, int causal, const int32_t* seqused_k, float scale,
+                 hipStream_t stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || out_fp4 == nullptr || out_sf == nullptr) return FA_ERR_NULL;
+  int rc = check_shape(B, Sq, Sk, Hq, Hkv, D, causal);
+  if (rc != FA_OK) return rc;
+  if (D % 16 != 0) return FA_ERR_UNSUPPORTED;  // blocks of 16 would straddle heads
+  if (!(scale > 0.0f) || !isfinite(scale)) return FA_ERR_SCALE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out_fp4, 4)) return FA_ERR_ALIGN;
+  if ((lse != nullptr && !aligned(lse, 4)) || (seqused_k != nullptr && !aligned(seqused_k, 4))) return FA_ERR_ALIGN;
+  const size_t rows = (size_t)B * Sq * Hq;
+  const size_t qb = rows * D * 2, kb = (size_t)B * Sk * Hkv * D * 2, cb = rows * D / 2, sb = rows * D / 16;
+  if (overlap(out_fp4, cb, q, qb) || overlap(out_fp4, cb, k, kb) || overlap(out_fp4, cb, v, kb) ||
+      overlap(out_sf, sb, q, qb) || overlap(out_sf, sb, k, kb) || overlap(out_sf, sb, v, kb) ||
+      overlap(out_fp4, cb, out_sf, sb))
+    return FA_ERR_ALIAS;
+  if (lse != nullptr) {
+    const size_t lb = rows * sizeof(float);
+    if (overlap(lse, lb, q, qb) || overlap(lse, lb, k, kb) || overlap(lse, lb, v, kb) ||
+        overlap(lse, lb, out_fp4, cb) || overlap(lse, lb, out_sf, sb))
+      return FA_ERR_ALIAS;
+  }
+  Plan pl = default_plan(B, Sq, Sk, Hq, Hkv, D, causal);
+  pl.launch.dtype = fa::kBf16;
+  pl.launch.outf = fa::kOutNvfp4;
+  if (!fa::nvfp4_variant_exists(pl.launch)) return FA_ERR_UNSUPPORTED;
+  return run(pl, q, k, v, nullptr, lse, B, Sq, Sk, Hq, Hkv, contiguous(Sq, Hq, D), contiguous(Sk, Hkv, D),
+             contiguous(Sk, Hkv, D), contiguous(Sq, Hq, D), seqused_k, scale, stream, Packed(), out_fp4, out_sf);
 }
 
 int fa_fwd_variant(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Sq, int Sk,

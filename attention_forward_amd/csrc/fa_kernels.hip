@@ -127,6 +127,72 @@ __device__ __forceinline__ float group_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// ---------------------------------------------------------- NVFP4 output
+// The attention output quantised for the output projection: per (token,
+// head) row, blocks of 16 head-dim elements; a block's scale is amax/6 in
+// fp32 rounded to UE4M3 (4-bit exponent bias 7, 3-bit mantissa, subnormals
+// m/8 * 2^-6, largest finite 448; nearest, ties to the even code,
+// saturating), and each element x / (decoded scale) in fp32 rounded to E2M1
+// (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6; nearest, ties to the even code,
+// saturating at 6; sign bit when x < 0).  A block whose scale rounds to zero
+// gets zero codes.  Two elements per byte, the even one in the low nibble.
+
+__device__ __forceinline__ uint32_t ue4m3_code(float v) {
+  if (!(v > 0.f)) return 0u;
+  if (v >= 448.f) return 0x7Eu;
+  const int e = (int)((__float_as_uint(v) >> 23) & 0xFF) - 127;  // floor(log2 v) for normal floats
+  if (e < -6) {
+    const float q = __builtin_rintf(v * 512.f);  // multiples of 2^-9, ties to even
+    return q >= 8.f ? 0x08u : (uint32_t)q;
+  }
+  float q = __builtin_rintf(__builtin_ldexpf(v, -e) * 8.f);  // mantissa in eighths: 8 .. 16
+  int ee = e;
+  if (q >= 16.f) {
+    q = 8.f;
+    ee += 1;
+  }
+  return ((uint32_t)(ee + 7) << 3) | ((uint32_t)q - 8u);
+}
+
+__device__ __forceinline__ float ue4m3_float(uint32_t c) {
+  const uint32_t e = c >> 3, m = c & 7u;
+  return e == 0 ? (float)m * 0.001953125f : __builtin_ldexpf(1.f + (float)m * 0.125f, (int)e - 7);
+}
+
+// E2M1 code of a quotient: the magnitude code counts the decision points
+// passed (strict at a midpoint whose lower neighbour has the even code).
+__device__ __forceinline__ uint32_t e2m1_code(float q) {
+  const float a = fabsf(q);
+  const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) + (uint32_t)(a >= 1.75f) +
+                     (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.f);
+  return c | (q < 0.f ? 8u : 0u);
+}
+
+// Scale code of a block from its amax, and the divisor its elements use
+// (0: the block is coded as zeros).
+__device__ __forceinline__ uint32_t nvfp4_scale(float amax, float& div) {
+  const uint32_t sc = ue4m3_code(amax / 6.f);
+  div = ue4m3_float(sc);
+  return sc;
+}
+
+// Four elements (x0..x3) of a block -> four nibbles (16 bits, x0 lowest).
+__device__ __forceinline__ uint32_t nvfp4_pack4(f32x4_t x, float div) {
+  if (!(div > 0.f)) return 0u;
+  return e2m1_code(x[0] / div) | (e2m1_code(x[1] / div) << 4) | (e2m1_code(x[2] / div) << 8) |
+         (e2m1_code(x[3] / div) << 12);
+}
+
+__device__ __forceinline__ float amax4(f32x4_t x) {
+  return fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
+}
+
+// Byte offset of (batch b, position s, head h)'s row in the NVFP4 output
+// (rows of D/2 code bytes; the scales use rows of D/16 bytes).
+__device__ __forceinline__ size_t nvfp4_row(const FwdParams& p, int b, int s, int h) {
+  return ((size_t)b * p.Sq + s) * p.Hq + h;
+}
+
 // One 16-byte copy per lane from a buffer to LDS (buffer_load_dwordx4 with
 // the LDS bit): lane i of the wave writes LDS bytes [lds + 16 i, +16) with
 // the 16 bytes at buffer offset voff, or zeros when that offset is past the
@@ -592,12 +658,13 @@ struct RowBlock {
   int kbeg, kend;
 };
 
-template <int D, int QT, int NW, int BN, int NST, int KG, bool CAUSAL, bool SPLIT, int DTY>
+template <int D, int QT, int NW, int BN, int NST, int KG, bool CAUSAL, bool SPLIT, int DTY, int OUTF>
 __global__ void __launch_bounds__(NW * KG * 64, 1)
 fwd_kernel(const FwdParams p) {
   using G = Geo<D, QT, NW, BN, DTY>;  // geometry of one key group: NW waves on different rows
   static_assert(NST >= 2, "at least double buffering");
   static_assert(KG == 1 || (KG == 2 && NST == 2), "two key groups run the two-stage loop");
+  static_assert(OUTF == kOutElem || D % 16 == 0, "NVFP4 blocks of 16 stay inside a head");
   static_assert(KG * NST * G::STAGE_B + (G::TRASH ? NW * KG * 1024 : 16) <= 160 * 1024, "LDS of one workgroup");
   __shared__ __attribute__((aligned(16))) uint8_t stage[KG * NST * G::STAGE_B];
   __shared__ __attribute__((aligned(16))) uint8_t trash[G::TRASH ? NW * KG * 1024 : 16];
@@ -883,14 +950,28 @@ fwd_kernel(const FwdParams p) {
       const int s = r / g, hh = r - s * g;
       const float l = l_tot[t];
       const float inv = (l > 0.f) ? 1.0f / l : 0.f;
-      uint16_t* op = p.out + view_off(b, sq.q0 + s, hk * g + hh, p.o_sb, p.o_ss, p.o_sh);
+      if constexpr (OUTF == kOutNvfp4) {
+        // Block dt is head-dim 16dt .. 16dt+15: four elements in each of the
+        // row's four lanes (l, l^16, l^32, l^48), whose amax group_max takes.
+        const size_t row = nvfp4_row(p, b, s, hk * g + hh);
 #pragma unroll
-      for (int dt = 0; dt < G::DT; ++dt) {
-        const int d = 16 * dt + 4 * grp;
-        if (d < D) {
-          u32x2_t w = {G::E::pack(oacc[dt][t][0] * inv, oacc[dt][t][1] * inv),
-                       G::E::pack(oacc[dt][t][2] * inv, oacc[dt][t][3] * inv)};
-          *reinterpret_cast<u32x2_t*>(op + d) = w;
+        for (int dt = 0; dt < G::DT; ++dt) {
+          const f32x4_t x = oacc[dt][t] * inv;
+          float div;
+          const uint32_t sc = nvfp4_scale(group_max(amax4(x)), div);
+          *reinterpret_cast<uint16_t*>(p.fp4_out + row * (D / 2) + 8 * dt + 2 * grp) = (uint16_t)nvfp4_pack4(x, div);
+          if (grp == 0) p.fp4_sf[row * (D / 16) + dt] = (uint8_t)sc;
+        }
+      } else {
+        uint16_t* op = p.out + view_off(b, sq.q0 + s, hk * g + hh, p.o_sb, p.o_ss, p.o_sh);
+#pragma unroll
+        for (int dt = 0; dt < G::DT; ++dt) {
+          const int d = 16 * dt + 4 * grp;
+          if (d < D) {
+            u32x2_t w = {G::E::pack(oacc[dt][t][0] * inv, oacc[dt][t][1] * inv),
+                         G::E::pack(oacc[dt][t][2] * inv, oacc[dt][t][3] * inv)};
+            *reinterpret_cast<u32x2_t*>(op + d) = w;
+          }
         }
       }
       if (p.lse != nullptr && grp == 0) {
@@ -932,7 +1013,7 @@ fwd_kernel(const FwdParams p) {
 // different rows and share tiles), a workgroup covers KW times fewer rows, so
 // a small number of rows still fills the chip, while each wave keeps 16*QT
 // rows against every K/V byte it reads from LDS.
-template <int D, int QT, int KW, int BN, bool CAUSAL, bool SPLIT, int DTY>
+template <int D, int QT, int KW, int BN, bool CAUSAL, bool SPLIT, int DTY, int OUTF>
 __global__ void __launch_bounds__(KW * 64, 1)
 fwd_ks_kernel(const FwdParams p) {
   using G = Geo<D, QT, 1, BN, DTY>;  // per-wave geometry: one wave issues its own tile copies
@@ -1173,7 +1254,18 @@ fwd_ks_kernel(const FwdParams p) {
           a0 += fw[w] * *reinterpret_cast<const f32x4_t*>(src);
           a1 += fw[w] * *reinterpret_cast<const f32x4_t*>(src + 16);
         }
-        if constexpr (!SPLIT) {
+        if constexpr (!SPLIT && OUTF == kOutNvfp4) {
+          // chunks ch and ch ^ 1 form a block of 16; the other one is in the
+          // neighbouring thread (tid ^ 1: same row, TPR even)
+          float am = fmaxf(amax4(a0), amax4(a1));
+          am = fmaxf(am, __shfl_xor(am, 1));
+          float div;
+          const uint32_t sc = nvfp4_scale(am, div);
+          const size_t row = nvfp4_row(p, b, s, hk * g + hh);
+          *reinterpret_cast<uint32_t*>(p.fp4_out + row * (D / 2) + 4 * ch) =
+              nvfp4_pack4(a0, div) | (nvfp4_pack4(a1, div) << 16);
+          if ((ch & 1) == 0) p.fp4_sf[row * (D / 16) + (ch >> 1)] = (uint8_t)sc;
+        } else if constexpr (!SPLIT) {
           const u32x4_t o = {G::E::pack(a0[0], a0[1]), G::E::pack(a0[2], a0[3]), G::E::pack(a1[0], a1[1]),
                              G::E::pack(a1[2], a1[3])};
           *reinterpret_cast<u32x4_t*>(p.out + view_off(b, sq.q0 + s, hk * g + hh, p.o_sb, p.o_ss, p.o_sh) + 8 * ch) = o;
@@ -1202,7 +1294,7 @@ fwd_ks_kernel(const FwdParams p) {
 //   M = max_z m_z over non-empty splits, w_z = l_z 2^(m_z - M),
 //   out = sum_z w_z Ohat_z / sum_z w_z,   lse = ln2 (M + log2 sum_z w_z).
 // The running form below rescales as M grows, which is the same sum.
-template <int D, int ROWS_WG, bool CAUSAL, int DTY>
+template <int D, int ROWS_WG, bool CAUSAL, int DTY, int OUTF>
 __global__ void __launch_bounds__(256)
 combine_kernel(const FwdParams p) {
   using E = Elem<DTY>;
@@ -1256,9 +1348,22 @@ combine_kernel(const FwdParams p) {
   }
   const int s = r / g, hh = r - s * g;
   const float inv = (L > 0.f) ? 1.0f / L : 0.f;
-  const u32x4_t o = {E::pack(a0[0] * inv, a0[1] * inv), E::pack(a0[2] * inv, a0[3] * inv),
-                     E::pack(a1[0] * inv, a1[1] * inv), E::pack(a1[2] * inv, a1[3] * inv)};
-  *reinterpret_cast<u32x4_t*>(p.out + view_off(b, sq.q0 + s, hk * g + hh, p.o_sb, p.o_ss, p.o_sh) + 8 * ch) = o;
+  if constexpr (OUTF == kOutNvfp4) {
+    // chunks ch and ch ^ 1 form a block of 16; the other one is in the
+    // neighbouring thread (index i ^ 1: same row, D/8 even)
+    const f32x4_t x0 = a0 * inv, x1 = a1 * inv;
+    float am = fmaxf(amax4(x0), amax4(x1));
+    am = fmaxf(am, __shfl_xor(am, 1));
+    float div;
+    const uint32_t sc = nvfp4_scale(am, div);
+    const size_t row = nvfp4_row(p, b, s, hk * g + hh);
+    *reinterpret_cast<uint32_t*>(p.fp4_out + row * (D / 2) + 4 * ch) = nvfp4_pack4(x0, div) | (nvfp4_pack4(x1, div) << 16);
+    if ((ch & 1) == 0) p.fp4_sf[row * (D / 16) + (ch >> 1)] = (uint8_t)sc;
+  } else {
+    const u32x4_t o = {E::pack(a0[0] * inv, a0[1] * inv), E::pack(a0[2] * inv, a0[3] * inv),
+                       E::pack(a1[0] * inv, a1[1] * inv), E::pack(a1[2] * inv, a1[3] * inv)};
+    *reinterpret_cast<u32x4_t*>(p.out + view_off(b, sq.q0 + s, hk * g + hh, p.o_sb, p.o_ss, p.o_sh) + 8 * ch) = o;
+  }
   if (ch == 0 && p.lse != nullptr) {
     const float lse = (L > 0.f) ? (M + __log2f(L)) * kLn2 : -INFINITY;
     p.lse[sq.lse0 + (long long)(hk * g + hh) * p.lse_hs + s] = lse;
@@ -1267,7 +1372,7 @@ combine_kernel(const FwdParams p) {
 
 // ------------------------------------------------------------------ launch
 
-template <int D, int QT, int NW, int BN, int NST, int KG, bool CAUSAL, bool SPLIT, int DTY>
+template <int D, int QT, int NW, int BN, int NST, int KG, bool CAUSAL, bool SPLIT, int DTY, int OUTF = kOutElem>
 static hipError_t launch_variant(const FwdParams& p, const LaunchPlan& plan, hipStream_t stream) {
   using G = Geo<D, QT, NW, BN, DTY>;
   const int nrb = (p.Mp + G::ROWS_WG - 1) / G::ROWS_WG;
@@ -1281,16 +1386,17 @@ static hipError_t launch_variant(const FwdParams& p, const LaunchPlan& plan, hip
   } else {
     grid = dim3(nrb, p.B * p.Hkv, SPLIT ? plan.nsplit : 1);
   }
-  hipLaunchKernelGGL((fwd_kernel<D, QT, NW, BN, NST, KG, CAUSAL, SPLIT, DTY>), grid, dim3(NW * KG * 64), 0, stream, p);
+  hipLaunchKernelGGL((fwd_kernel<D, QT, NW, BN, NST, KG, CAUSAL, SPLIT, DTY, OUTF>), grid, dim3(NW * KG * 64), 0, stream,
+                     p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !SPLIT) return e;
   const long long threads = (long long)p.B * p.Hkv * nrb * G::ROWS_WG * (D / 8);
-  hipLaunchKernelGGL((combine_kernel<D, G::ROWS_WG, CAUSAL, DTY>), dim3((unsigned)((threads + 255) / 256)),
+  hipLaunchKernelGGL((combine_kernel<D, G::ROWS_WG, CAUSAL, DTY, OUTF>), dim3((unsigned)((threads + 255) / 256)),
                      dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
-template <int D, int QT, int KW, int BN, bool CAUSAL, bool SPLIT, int DTY>
+template <int D, int QT, int KW, int BN, bool CAUSAL, bool SPLIT, int DTY, int OUTF = kOutElem>
 static hipError_t launch_ks_variant(const FwdParams& p, const LaunchPlan& plan, hipStream_t stream) {
   constexpr int ROWS = 16 * QT;
   const int nrb = (p.Mp + ROWS - 1) / ROWS;
@@ -1304,11 +1410,11 @@ static hipError_t launch_ks_variant(const FwdParams& p, const LaunchPlan& plan, 
   } else {
     grid = dim3(nrb, p.B * p.Hkv, SPLIT ? plan.nsplit : 1);
   }
-  hipLaunchKernelGGL((fwd_ks_kernel<D, QT, KW, BN, CAUSAL, SPLIT, DTY>), grid, dim3(KW * 64), 0, stream, p);
+  hipLaunchKernelGGL((fwd_ks_kernel<D, QT, KW, BN, CAUSAL, SPLIT, DTY, OUTF>), grid, dim3(KW * 64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !SPLIT) return e;
   const long long threads = (long long)p.B * p.Hkv * nrb * ROWS * (D / 8);
-  hipLaunchKernelGGL((combine_kernel<D, ROWS, CAUSAL, DTY>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+  hipLaunchKernelGGL((combine_kernel<D, ROWS, CAUSAL, DTY, OUTF>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
                      stream, p);
   return hipGetLastError();
 }
@@ -1374,7 +1480,26 @@ bool variant_exists(int D, int qt, int nw, int kw, int bn, int nst, int dtype) {
   return false;
 }
 
+// NVFP4 output: built for the default bf16 plans of the head dims whose rows
+// split into whole blocks of 16 (row-split at 64, key-split at 256).
+bool nvfp4_variant_exists(const LaunchPlan& l) {
+  return l.dtype == kBf16 && ((l.D == 64 && l.qt == 1 && l.nw == 4 && l.kw == 1 && l.bn == 64 && l.nst == 2) ||
+                              (l.D == 256 && l.qt == 2 && l.nw == 4 && l.kw == 4 && l.bn == 32 && l.nst == 1));
+}
+
+template <bool CAUSAL, bool SPLIT>
+static hipError_t launch_nvfp4(const FwdParams& p, const LaunchPlan& plan, hipStream_t stream) {
+  if (plan.D == 64) return launch_variant<64, 1, 4, 64, 2, 1, CAUSAL, SPLIT, kBf16, kOutNvfp4>(p, plan, stream);
+  return launch_ks_variant<256, 2, 4, 32, CAUSAL, SPLIT, kBf16, kOutNvfp4>(p, plan, stream);
+}
+
 hipError_t launch_fwd(const FwdParams& p, const LaunchPlan& plan, hipStream_t stream) {
+  if (plan.outf == kOutNvfp4) {
+    if (!nvfp4_variant_exists(plan)) return hipErrorInvalidValue;
+    if (plan.causal)
+      return plan.split ? launch_nvfp4<true, true>(p, plan, stream) : launch_nvfp4<true, false>(p, plan, stream);
+    return plan.split ? launch_nvfp4<false, true>(p, plan, stream) : launch_nvfp4<false, false>(p, plan, stream);
+  }
   if (plan.kw > 1 && plan.kw == plan.nw) {
 #define FA_KS_DISPATCH(t_, d_, q_, k_, b_)                                                          \
   if (plan.dtype == t_ && plan.D == d_ && plan.qt == q_ && plan.kw == k_ && plan.bn == b_) {         \

@@ -13,6 +13,10 @@ struct FwdParams {
   const uint16_t* k;       // (batch, key, kv head, head_dim) view
   const uint16_t* v;       // (batch, key, kv head, head_dim) view
   uint16_t* out;           // (batch, position, head, head_dim) view, written
+  // NVFP4 output instead of out (the NVFP4 variants): per (batch, position,
+  // head) row, contiguous, D/2 bytes of E2M1 pairs and D/16 UE4M3 scales.
+  uint8_t* fp4_out;
+  uint8_t* fp4_sf;
   float* lse;              // [B, Hq, Sq] fp32 contiguous, or null
   const int32_t* seqused;  // [B] int32 on the device, or null
   // Packed variable-length batch (both null otherwise): B + 1 offsets each,
@@ -45,6 +49,7 @@ struct FwdParams {
 };
 
 enum ElemType { kBf16 = 0, kF16 = 1 };
+enum OutFormat { kOutElem = 0, kOutNvfp4 = 1 };  // out in the element type, or NVFP4
 
 struct LaunchPlan {
   int D;
@@ -57,9 +62,11 @@ struct LaunchPlan {
   bool split;
   int nsplit;              // non-causal split count (grid.z)
   int dtype;               // ElemType of q, k, v and out
+  int outf;                // OutFormat of the result
 };
 
 bool variant_exists(int D, int qt, int nw, int kw, int bn, int nst, int dtype);
+bool nvfp4_variant_exists(const LaunchPlan& plan);
 hipError_t launch_fwd(const FwdParams& p, const LaunchPlan& plan, hipStream_t stream);
 
 }  // namespace fa

@@ -33,7 +33,8 @@ FA_ERR_ALIAS = 8
 FA_BF16 = 0
 FA_FP16 = 1
 
-EXPORTS = ("fa_fwd", "fa_fwd_strided", "fa_fwd_varlen", "fa_fwd_workspace_bytes", "fa_set_workspace", "fa_fwd_variant",
+EXPORTS = ("fa_fwd", "fa_fwd_strided", "fa_fwd_varlen", "fa_fwd_nvfp4", "fa_fwd_workspace_bytes", "fa_set_workspace",
+           "fa_fwd_variant",
            "fa_fwd_variant_workspace_bytes", "fa_fwd_plan", "fa_status_string", "fa_abi_version")
 
 _lib = None
@@ -67,6 +68,8 @@ def load_library():
         lib.fa_fwd_strided.argtypes = [vp, vp, vp, vp, vp] + [i32] * 6 + [i64] * 12 + [i32, i32, vp, f32, vp]
         lib.fa_fwd_varlen.restype = i32
         lib.fa_fwd_varlen.argtypes = [vp] * 7 + [i32] * 10 + [f32, vp]
+        lib.fa_fwd_nvfp4.restype = i32
+        lib.fa_fwd_nvfp4.argtypes = [vp] * 6 + [i32] * 7 + [vp, f32, vp]
         lib.fa_fwd_workspace_bytes.restype = ctypes.c_size_t
         lib.fa_fwd_workspace_bytes.argtypes = [i32] * 7
         lib.fa_set_workspace.restype = i32
@@ -113,6 +116,13 @@ def fa_fwd_varlen(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, B, max_seqlen_q
                                         cu_seqlens_q or None, cu_seqlens_k or None, B, max_seqlen_q, max_seqlen_k,
                                         total_q, total_k, Hq, Hkv, D, int(dtype), int(causal),
                                         ctypes.c_float(scale), stream or None)
+
+
+def fa_fwd_nvfp4(q, k, v, out_fp4, out_sf, lse, B, Sq, Sk, Hq, Hkv, D, causal, seqused_k, scale, stream) -> int:
+    """C ``fa_fwd_nvfp4``; pointers and stream are integers (0 for NULL)."""
+    return load_library().fa_fwd_nvfp4(q or None, k or None, v or None, out_fp4 or None, out_sf or None, lse or None,
+                                       B, Sq, Sk, Hq, Hkv, D, int(causal), seqused_k or None,
+                                       ctypes.c_float(scale), stream or None)
 
 
 def fa_fwd_workspace_bytes(B, Sq, Sk, Hq, Hkv, D, causal) -> int:
@@ -247,6 +257,58 @@ def attention(q, k, v, *, causal=False, seqused_k=None, scale=None, out=None, ls
     if rc != FA_OK:
         raise FAError(rc, where)
     return out, lse
+
+
+def attention_nvfp4(q, k, v, *, causal=False, seqused_k=None, scale=None, out_fp4=None, out_sf=None, lse=None,
+                    return_lse=True):
+    """Attention with the output quantised to NVFP4 in the same launch
+    (fa_fwd_nvfp4): contiguous bfloat16 q [B, Sq, Hq, D], k, v [B, Sk, Hkv, D]
+    with D 64 or 256.  Returns (codes uint8 [B, Sq, Hq, D/2], scales uint8
+    [B, Sq, Hq, D/16], lse [B, Hq, Sq] float32 or None)."""
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+            raise TypeError(f"{name} must be a contiguous bfloat16 cuda tensor")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D (batch, seq, heads, head_dim)")
+    B, Sq, Hq, D = q.shape
+    Bk, Sk, Hkv, Dk = k.shape
+    if tuple(v.shape) != tuple(k.shape) or Bk != B or Dk != D:
+        raise ValueError("k and v must be [B, Sk, Hkv, D] matching q")
+    dev = q.device
+    if k.device != dev or v.device != dev:
+        raise ValueError("q, k, v must be on one device")
+    if D % 16 != 0:
+        raise ValueError("NVFP4 output needs a head dim that is a multiple of 16")
+    if seqused_k is not None and (seqused_k.dtype != torch.int32 or seqused_k.device != dev
+                                  or seqused_k.numel() != B or not seqused_k.is_contiguous()):
+        raise ValueError("seqused_k must be a contiguous int32 tensor of B entries on q's device")
+    shapes = {"out_fp4": (B, Sq, Hq, D // 2), "out_sf": (B, Sq, Hq, D // 16)}
+    bufs = {"out_fp4": out_fp4, "out_sf": out_sf}
+    for name, t in bufs.items():
+        if t is None:
+            bufs[name] = torch.empty(shapes[name], dtype=torch.uint8, device=dev)
+        elif tuple(t.shape) != shapes[name] or t.dtype != torch.uint8 or t.device != dev or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous uint8 tensor of shape {shapes[name]}")
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev)
+    elif lse is not None and (tuple(lse.shape) != (B, Hq, Sq) or lse.dtype != torch.float32
+                              or lse.device != dev or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 [B, Hq, Sq] tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    causal = bool(causal)
+    sq = 0 if seqused_k is None else seqused_k.data_ptr()
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        ensure_workspace(dev, fa_fwd_workspace_bytes(B, Sq, Sk, Hq, Hkv, D, causal))
+        rc = fa_fwd_nvfp4(q.data_ptr(), k.data_ptr(), v.data_ptr(), bufs["out_fp4"].data_ptr(),
+                          bufs["out_sf"].data_ptr(), 0 if lse is None else lse.data_ptr(), B, Sq, Sk, Hq, Hkv, D,
+                          causal, sq, float(scale), stream)
+    if rc != FA_OK:
+        raise FAError(rc, "fa_fwd_nvfp4")
+    return bufs["out_fp4"], bufs["out_sf"], lse
 
 
 def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, *, causal=False,

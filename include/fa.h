@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 3
+#define FA_ABI_VERSION 4
 
 /* Status codes. */
 enum {
@@ -186,6 +186,32 @@ size_t fa_fwd_workspace_bytes(int B, int Sq, int Sk, int Hq, int Hkv, int D, int
  * Returns FA_OK, FA_ERR_NULL for a NULL pointer with bytes > 0, or
  * FA_ERR_LAUNCH when no HIP device is current. */
 int fa_set_workspace(void* dev_ptr, size_t bytes);
+
+/* fa_fwd_nvfp4: fa_fwd with the output quantised to NVFP4 for the output
+ * projection, in the same launch ("pi05_thor_decoder_fp4_e2e.md", section
+ * "Implemented Path": dynamic NVFP4 quantisation of the attention output
+ * before O; "GROOT N1.7 update: Thor NVFP4 + FA4 performance tier", section
+ * "What is in the tier": per-16-element, no calibration; the same page as
+ * the first, section "E0M3 Uniform-INT4 Decoder Weights": per-16 UE4M3
+ * scales at amax over the grid maximum).
+ *   out_fp4  [B, Sq, Hq, D/2] bytes, written: the E2M1 codes of each
+ *            (token, head) row, element 2i in the low nibble of byte i
+ *            (4-byte aligned)
+ *   out_sf   [B, Sq, Hq, D/16] bytes, written: one UE4M3 scale per 16
+ *            consecutive head-dim elements
+ * A block's scale is amax/6 (fp32) rounded to UE4M3 (nearest, ties to the
+ * even code, at most 448); its elements are x / (decoded scale) (fp32)
+ * rounded to E2M1 (nearest, ties to the even code, at most 6 in magnitude;
+ * sign bit when x < 0), x the fp32 attention output before any rounding;
+ * a scale that rounds to zero gives zero codes.  q, k, v are bf16 and
+ * contiguous; D must be 64 or 256 (a multiple of 16 with a compiled
+ * variant; FA_ERR_UNSUPPORTED otherwise).  Everything else (lse,
+ * seqused_k, causal, scale, stream, workspace, checks and codes) is as for
+ * fa_fwd; out_fp4, out_sf and lse must not overlap each other or q, k, v
+ * (FA_ERR_ALIAS). */
+int fa_fwd_nvfp4(const void* q, const void* k, const void* v, void* out_fp4, void* out_sf, float* lse,
+                 int B, int Sq, int Sk, int Hq, int Hkv, int D, int causal,
+                 const int32_t* seqused_k, float scale, hipStream_t stream);
 
 /* Tuning and testing entry points.  fa_fwd picks its kernel variant from
  * the shape alone; these name one explicitly so that every compiled variant

@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert fa.fa_abi_version() == 3
+    assert fa.fa_abi_version() == 4
     for code in range(9):
         assert fa.fa_status_string(code).startswith("FA_")
     assert "UNKNOWN" in fa.fa_status_string(99)
@@ -233,6 +233,37 @@ def test_variant_rejections(lib):
     bad = list(args)
     bad[0] = 0
     assert fa.fa_fwd_variant(*bad, 1, 4, 1, 32, 2, 0, 0) == fa.FA_ERR_NULL
+
+
+def _call_nvfp4(**over):
+    """fa_fwd_nvfp4 with valid defaults (fake device addresses: nothing is
+    launched, every case fails a host check first)."""
+    a = dict(q=Q, k=K, v=V, fp4=O, sf=O + (1 << 24), lse=L, B=1, Sq=64, Sk=64, Hq=8, Hkv=1, D=256, causal=0,
+             seqused_k=0, scale=0.0625, stream=0)
+    a.update(over)
+    return fa.fa_fwd_nvfp4(a["q"], a["k"], a["v"], a["fp4"], a["sf"], a["lse"], a["B"], a["Sq"], a["Sk"], a["Hq"],
+                           a["Hkv"], a["D"], a["causal"], a["seqused_k"], a["scale"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=0), fa.FA_ERR_NULL),
+    (dict(fp4=0), fa.FA_ERR_NULL),
+    (dict(sf=0), fa.FA_ERR_NULL),
+    (dict(B=0), fa.FA_ERR_SHAPE),
+    (dict(Hq=6, Hkv=4), fa.FA_ERR_SHAPE),
+    (dict(D=72, Hq=16, Hkv=16), fa.FA_ERR_UNSUPPORTED),   # blocks of 16 would straddle heads
+    (dict(D=128), fa.FA_ERR_UNSUPPORTED),
+    (dict(scale=0.0), fa.FA_ERR_SCALE),
+    (dict(fp4=O + 2), fa.FA_ERR_ALIGN),
+    (dict(q=Q + 8), fa.FA_ERR_ALIGN),
+    (dict(lse=L + 2), fa.FA_ERR_ALIGN),
+    (dict(fp4=Q), fa.FA_ERR_ALIAS),
+    (dict(sf=K + 64), fa.FA_ERR_ALIAS),
+    (dict(sf=O + 1024), fa.FA_ERR_ALIAS),            # inside the codes (64 rows x 128 bytes)
+    (dict(lse=O + 4096), fa.FA_ERR_ALIAS),
+])
+def test_nvfp4_invalid_arguments_return_their_code(lib, over, code):
+    assert _call_nvfp4(**over) == code
 
 
 def test_set_workspace_null_with_size(lib):
