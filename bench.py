@@ -329,7 +329,7 @@ def extension_rows(device, steps=200):
     """µs per call of the extended entry points on shapes taken from the
     workloads: fp16, a fused QKV buffer read in place, a packed
     variable-length batch, a causal chunk of new positions attending a cache,
-    and causal decode over the padded prefix cache."""
+    causal decode over the padded prefix cache, and the NVFP4 output."""
     import torch
     from attention_forward_amd import fa
     from attention_forward_amd.workloads import make_custom
@@ -390,6 +390,22 @@ def extension_rows(device, steps=200):
             sq.data_ptr(), 0.0625)
     record("causal_decode_1x1009_gqa", lambda h, a=args: fa.fa_fwd(*a, h), 4 * Dd * Hq * n,
            (2 * Sq * Hq + 2 * n) * Dd * 2 + Hq * Sq * 4)
+    # NVFP4 output (fa_fwd_nvfp4) on the two D256 GQA workloads: the output is
+    # D/2 code bytes and D/16 scale bytes per row instead of 2D
+    from attention_forward_amd.workloads import WORKLOADS, make_inputs
+    for name in ("prefix_gqa_padded", "action_expert_small_m"):
+        w = WORKLOADS[name]
+        q, k, v, sq = (t.to(device) if t is not None else None for t in make_inputs(name))
+        codes = torch.empty(w.B, w.Sq, w.Hq, w.D // 2, dtype=torch.uint8, device=device)
+        sf = torch.empty(w.B, w.Sq, w.Hq, w.D // 16, dtype=torch.uint8, device=device)
+        lse = torch.empty(w.B, w.Hq, w.Sq, dtype=torch.float32, device=device)
+        fa.ensure_workspace(q.device, fa.fa_fwd_workspace_bytes(w.B, w.Sq, w.Sk, w.Hq, w.Hkv, w.D, w.causal))
+        args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), codes.data_ptr(), sf.data_ptr(), lse.data_ptr(), w.B, w.Sq,
+                w.Sk, w.Hq, w.Hkv, w.D, int(w.causal), 0 if sq is None else sq.data_ptr(), w.scale)
+        flops, nbytes = algorithmic(w)
+        rows_q = w.B * w.Sq * w.Hq
+        record(f"{name}_nvfp4", lambda h, a=args: fa.fa_fwd_nvfp4(*a, h), flops,
+               nbytes - rows_q * w.D * 2 + rows_q * (w.D // 2 + w.D // 16))
     return rows
 
 
