@@ -134,7 +134,8 @@ __device__ __forceinline__ float group_sum(float x) {
 // m/8 * 2^-6, largest finite 448; nearest, ties to the even code,
 // saturating), and each element x / (decoded scale) in fp32 rounded to E2M1
 // (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6; nearest, ties to the even code,
-// saturating at 6; sign bit when x < 0).  A block whose scale rounds to zero
+// saturating at 6; sign bit when x < 0), decided without the division
+// (e2m1_cuts).  A block whose scale rounds to zero
 // gets zero codes.  Two elements per byte, the even one in the low nibble.
 
 __device__ __forceinline__ uint32_t ue4m3_code(float v) {
@@ -159,28 +160,44 @@ __device__ __forceinline__ float ue4m3_float(uint32_t c) {
   return e == 0 ? (float)m * 0.001953125f : __builtin_ldexpf(1.f + (float)m * 0.125f, (int)e - 7);
 }
 
-// E2M1 code of a quotient: the magnitude code counts the decision points
-// passed (strict at a midpoint whose lower neighbour has the even code).
-__device__ __forceinline__ uint32_t e2m1_code(float q) {
-  const float a = fabsf(q);
-  const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) + (uint32_t)(a >= 1.75f) +
-                     (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.f);
-  return c | (q < 0.f ? 8u : 0u);
+// E2M1 decision points of a block: the midpoints between neighbouring
+// magnitudes (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5) times the decoded scale.
+// Each product is exact (a short dyadic times a scale of at most 4
+// significant bits), and an fp32 x that is not exactly such a product is
+// more than half an ulp of the midpoint away from it after division, so
+// comparing |x| with the products decides exactly as rounding the fp32
+// quotient x / scale and comparing that with the midpoints.
+struct E2m1Cuts {
+  float c[7];
+};
+
+__device__ __forceinline__ E2m1Cuts e2m1_cuts(float scale) {
+  return E2m1Cuts{{0.25f * scale, 0.75f * scale, 1.25f * scale, 1.75f * scale, 2.5f * scale, 3.5f * scale,
+                   5.f * scale}};
 }
 
-// Scale code of a block from its amax, and the divisor its elements use
-// (0: the block is coded as zeros).
-__device__ __forceinline__ uint32_t nvfp4_scale(float amax, float& div) {
+// E2M1 code: the magnitude code counts the decision points passed (strict at
+// a midpoint whose lower neighbour has the even code).
+__device__ __forceinline__ uint32_t e2m1_code(float x, const E2m1Cuts& k) {
+  const float a = fabsf(x);
+  const uint32_t c = (uint32_t)(a > k.c[0]) + (uint32_t)(a >= k.c[1]) + (uint32_t)(a > k.c[2]) +
+                     (uint32_t)(a >= k.c[3]) + (uint32_t)(a > k.c[4]) + (uint32_t)(a >= k.c[5]) + (uint32_t)(a > k.c[6]);
+  return c | (x < 0.f ? 8u : 0u);
+}
+
+// Scale code of a block from its amax, and the decoded scale its elements
+// use (0: the block is coded as zeros).
+__device__ __forceinline__ uint32_t nvfp4_scale(float amax, float& scale) {
   const uint32_t sc = ue4m3_code(amax / 6.f);
-  div = ue4m3_float(sc);
+  scale = ue4m3_float(sc);
   return sc;
 }
 
 // Four elements (x0..x3) of a block -> four nibbles (16 bits, x0 lowest).
-__device__ __forceinline__ uint32_t nvfp4_pack4(f32x4_t x, float div) {
-  if (!(div > 0.f)) return 0u;
-  return e2m1_code(x[0] / div) | (e2m1_code(x[1] / div) << 4) | (e2m1_code(x[2] / div) << 8) |
-         (e2m1_code(x[3] / div) << 12);
+__device__ __forceinline__ uint32_t nvfp4_pack4(f32x4_t x, float scale) {
+  if (!(scale > 0.f)) return 0u;
+  const E2m1Cuts k = e2m1_cuts(scale);
+  return e2m1_code(x[0], k) | (e2m1_code(x[1], k) << 4) | (e2m1_code(x[2], k) << 8) | (e2m1_code(x[3], k) << 12);
 }
 
 __device__ __forceinline__ float amax4(f32x4_t x) {
