@@ -1306,7 +1306,7 @@ fwd_ks_kernel(const FwdParams p) {
   }
 }
 
-// Merge of the split-KV partials of one packed row and 8 head-dim elements
+// Merge of the split-KV partials of one packed row and 4 head-dim elements
 // per thread, in split order (deterministic):
 //   M = max_z m_z over non-empty splits, w_z = l_z 2^(m_z - M),
 //   out = sum_z w_z Ohat_z / sum_z w_z,   lse = ln2 (M + log2 sum_z w_z).
@@ -1315,7 +1315,7 @@ template <int D, int ROWS_WG, bool CAUSAL, int DTY, int OUTF>
 __global__ void __launch_bounds__(256)
 combine_kernel(const FwdParams p) {
   using E = Elem<DTY>;
-  constexpr int CPR = D / 8;
+  constexpr int CPR = D / 4;  // 4-element chunks per row: one per thread
   const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
   const long long per_bh = (long long)p.nrb * ROWS_WG * CPR;
   const int bh = (int)(i / per_bh);
@@ -1335,19 +1335,17 @@ combine_kernel(const FwdParams p) {
   }
   const size_t slot_base = ((size_t)bh * p.nrb + rb) * p.zmax;
   float M = -INFINITY, L = 0.f;
-  f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-  constexpr int U = 4;  // splits whose loads are in flight together
+  f32x4_t a = {0.f, 0.f, 0.f, 0.f};
+  constexpr int U = 8;  // splits whose loads are in flight together
   for (int z0 = 0; z0 < nz; z0 += U) {
     u32x2_t ml[U];
-    f32x4_t o0[U], o1[U];
+    f32x4_t o[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int z = min(z0 + u, nz - 1);
       const size_t prow = (slot_base + z) * ROWS_WG + rl;
       ml[u] = *reinterpret_cast<const u32x2_t*>(p.ws_ml + 2 * prow);
-      const f32x4_t* po = reinterpret_cast<const f32x4_t*>(p.ws_o + prow * D + 8 * ch);
-      o0[u] = po[0];
-      o1[u] = po[1];
+      o[u] = *reinterpret_cast<const f32x4_t*>(p.ws_o + prow * D + 4 * ch);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -1358,28 +1356,27 @@ combine_kernel(const FwdParams p) {
       const float alpha = __builtin_amdgcn_exp2f(M - m_new);  // 0 while M = -inf
       const float w = lz * __builtin_amdgcn_exp2f(mz - m_new);
       L = L * alpha + w;
-      a0 = a0 * alpha + w * o0[u];
-      a1 = a1 * alpha + w * o1[u];
+      a = a * alpha + w * o[u];
       M = m_new;
     }
   }
   const int s = r / g, hh = r - s * g;
   const float inv = (L > 0.f) ? 1.0f / L : 0.f;
   if constexpr (OUTF == kOutNvfp4) {
-    // chunks ch and ch ^ 1 form a block of 16; the other one is in the
-    // neighbouring thread (index i ^ 1: same row, D/8 even)
-    const f32x4_t x0 = a0 * inv, x1 = a1 * inv;
-    float am = fmaxf(amax4(x0), amax4(x1));
+    // a block of 16 is chunks 4j .. 4j+3, held by threads i with the same
+    // i >> 2 (same row: D/4 is a multiple of 4)
+    const f32x4_t x = a * inv;
+    float am = amax4(x);
     am = fmaxf(am, __shfl_xor(am, 1));
+    am = fmaxf(am, __shfl_xor(am, 2));
     float div;
     const uint32_t sc = nvfp4_scale(am, div);
     const size_t row = nvfp4_row(p, b, s, hk * g + hh);
-    *reinterpret_cast<uint32_t*>(p.fp4_out + row * (D / 2) + 4 * ch) = nvfp4_pack4(x0, div) | (nvfp4_pack4(x1, div) << 16);
-    if ((ch & 1) == 0) p.fp4_sf[row * (D / 16) + (ch >> 1)] = (uint8_t)sc;
+    *reinterpret_cast<uint16_t*>(p.fp4_out + row * (D / 2) + 2 * ch) = (uint16_t)nvfp4_pack4(x, div);
+    if ((ch & 3) == 0) p.fp4_sf[row * (D / 16) + (ch >> 2)] = (uint8_t)sc;
   } else {
-    const u32x4_t o = {E::pack(a0[0] * inv, a0[1] * inv), E::pack(a0[2] * inv, a0[3] * inv),
-                       E::pack(a1[0] * inv, a1[1] * inv), E::pack(a1[2] * inv, a1[3] * inv)};
-    *reinterpret_cast<u32x4_t*>(p.out + view_off(b, sq.q0 + s, hk * g + hh, p.o_sb, p.o_ss, p.o_sh) + 8 * ch) = o;
+    const u32x2_t o = {E::pack(a[0] * inv, a[1] * inv), E::pack(a[2] * inv, a[3] * inv)};
+    *reinterpret_cast<u32x2_t*>(p.out + view_off(b, sq.q0 + s, hk * g + hh, p.o_sb, p.o_ss, p.o_sh) + 4 * ch) = o;
   }
   if (ch == 0 && p.lse != nullptr) {
     const float lse = (L > 0.f) ? (M + __log2f(L)) * kLn2 : -INFINITY;
@@ -1407,7 +1404,7 @@ static hipError_t launch_variant(const FwdParams& p, const LaunchPlan& plan, hip
                      p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !SPLIT) return e;
-  const long long threads = (long long)p.B * p.Hkv * nrb * G::ROWS_WG * (D / 8);
+  const long long threads = (long long)p.B * p.Hkv * nrb * G::ROWS_WG * (D / 4);
   hipLaunchKernelGGL((combine_kernel<D, G::ROWS_WG, CAUSAL, DTY, OUTF>), dim3((unsigned)((threads + 255) / 256)),
                      dim3(256), 0, stream, p);
   return hipGetLastError();
@@ -1430,7 +1427,7 @@ static hipError_t launch_ks_variant(const FwdParams& p, const LaunchPlan& plan, 
   hipLaunchKernelGGL((fwd_ks_kernel<D, QT, KW, BN, CAUSAL, SPLIT, DTY, OUTF>), grid, dim3(KW * 64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !SPLIT) return e;
-  const long long threads = (long long)p.B * p.Hkv * nrb * ROWS * (D / 8);
+  const long long threads = (long long)p.B * p.Hkv * nrb * ROWS * (D / 4);
   hipLaunchKernelGGL((combine_kernel<D, ROWS, CAUSAL, DTY, OUTF>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
                      stream, p);
   return hipGetLastError();
