@@ -116,6 +116,12 @@ Plan default_plan(int B, int Sq, int Sk, int Hq, int Hkv, int D, int causal) {
   }
   const int rows = rows_per_block(pl.launch);
   const long long base = cdiv(Mp, rows) * BH;
+  // Row-split: 128-key tiles (half the trips, barriers and row reductions
+  // per key) when the single-pass grid fits the compute units in one round
+  // and the buffer holds at least one such tile.  Their 96 KB of stages allow
+  // one workgroup per compute unit, so larger grids keep 64-key tiles, with
+  // which two or three workgroups share a compute unit.
+  if (D != 256 && base <= kTargetWorkgroups && Sk >= 128) pl.launch.bn = 128;
   pl.kps = 0;
   if (base <= kTargetWorkgroups / 2) {
     const int kps = base <= 32 ? 128 : (base <= 64 ? 256 : 512);

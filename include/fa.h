@@ -224,7 +224,7 @@ int fa_fwd_nvfp4(const void* q, const void* k, const void* v, void* out_fp4, voi
  *        2 with nw = 4 or 8: two groups of nw/2 wavefronts on the same
  *        rows, each group sharing its own K/V tiles and taking every other
  *        key tile, merged at the end (nst 2)
- *   bn   keys per tile             (32 or 64)
+ *   bn   keys per tile             (32, 64 or 128)
  *   nst  K/V tile stages in LDS    (1, 2, 3 or 4)
  *   kps  keys per split-KV range   (0: single pass; else a multiple of bn)
  * A combination that is not compiled returns FA_ERR_UNSUPPORTED.  Other

@@ -214,7 +214,9 @@ def test_plan_kernel_choice(lib):
     assert fa.fa_fwd_plan(1, 41, 1056, 8, 1, 256, 0) == (2, 4, 4, 32, 1, 128)
     assert fa.fa_fwd_plan(1, 512, 512, 8, 1, 256, 0) == (2, 4, 4, 32, 1, 0)   # 128 blocks: no split
     # Smaller head dims: row-split workgroups, 16 rows per wave
-    assert fa.fa_fwd_plan(3, 256, 256, 16, 16, 72, 0) == (1, 4, 1, 64, 2, 0)
+    assert fa.fa_fwd_plan(3, 256, 256, 16, 16, 72, 0) == (1, 4, 1, 128, 2, 0)   # 192 blocks: 128-key tiles
+    assert fa.fa_fwd_plan(6, 256, 256, 16, 16, 72, 0) == (1, 4, 1, 64, 2, 0)    # 384 blocks: 64-key tiles
+    assert fa.fa_fwd_plan(2, 77, 77, 16, 16, 72, 1) == (1, 4, 1, 64, 2, 0)      # fewer than 128 keys
     assert fa.fa_fwd_plan(1, 64, 64, 1, 1, 64, 0) == (1, 4, 1, 64, 2, 0)
 
 

@@ -19,7 +19,7 @@ pytestmark = pytest.mark.gpu
 # waves own different rows and share K/V tiles; kw = nw: waves share rows and
 # split the keys (each streams its own tiles, nst = 1); kw = 2 < nw: two key
 # groups of nw/2 waves, each group sharing its own tiles, merged at the end.
-VARIANTS = [(64, 1, 4, 1, 64, 2), (64, 1, 4, 1, 64, 3), (64, 2, 2, 1, 64, 2), (64, 2, 4, 1, 64, 2),
+VARIANTS = [(64, 1, 4, 1, 64, 2), (64, 1, 4, 1, 128, 2), (72, 1, 4, 1, 128, 2), (64, 1, 4, 1, 64, 3), (64, 2, 2, 1, 64, 2), (64, 2, 4, 1, 64, 2),
             (72, 1, 4, 1, 64, 2), (72, 1, 4, 1, 64, 3), (72, 1, 4, 1, 64, 4), (72, 2, 2, 1, 64, 2), (72, 2, 2, 1, 64, 3), (72, 2, 4, 1, 64, 2), (256, 1, 4, 1, 32, 2), (256, 1, 4, 1, 32, 4), (256, 1, 4, 1, 64, 2),
             (256, 2, 4, 1, 32, 2), (256, 2, 4, 1, 32, 4), (256, 2, 4, 1, 64, 2),
             (64, 2, 4, 4, 64, 1), (72, 2, 4, 4, 64, 1), (256, 2, 4, 4, 32, 1), (256, 2, 2, 2, 32, 1),
