@@ -621,6 +621,21 @@ __host__ __device__ __forceinline__ int causal_kmax(int rb, int rows, int Mp, in
   return k < 0 ? 0 : (k > Sk ? Sk : k);
 }
 
+// Causal grids: workgroup x takes row block nrb - 1 - x / zmax (heaviest
+// first) and key range x % zmax of it (zmax = 1 without splitting).  Returns
+// false for a key range past the block's last planned key: such a workgroup
+// has no work, and the merge reads no partial from it.
+template <bool SPLIT>
+__device__ __forceinline__ bool causal_item(const FwdParams& p, int rows, int g, int& rb, int& z, int& kmax) {
+  const int nrb = (p.Mp + rows - 1) / rows;
+  const int x = blockIdx.x;
+  const int q = SPLIT ? x / p.zmax : x;
+  rb = nrb - 1 - q;
+  z = SPLIT ? x - q * p.zmax : 0;
+  kmax = causal_kmax(rb, rows, p.Mp, g, p.coff, p.Sk);
+  return !SPLIT || z * p.kps < kmax;
+}
+
 // Element offset b*sb + r*ss + h*sh of a (batch, position, head) view.
 // Indices and strides are non-negative and the host keeps the position and
 // head strides below 2^31, so those two terms are 32x32-bit products; only
@@ -714,18 +729,10 @@ fwd_kernel(const FwdParams p) {
   // Which rows and keys this workgroup takes.
   RowBlock blk;
   if constexpr (CAUSAL) {
-    // Heaviest row blocks first: walk from the last block down.
-    const int nrb = (p.Mp + G::ROWS_WG - 1) / G::ROWS_WG;
-    int item = blockIdx.x, rb = nrb - 1;
-    for (; rb >= 0; --rb) {
-      const int kmax = causal_kmax(rb, G::ROWS_WG, p.Mp, g, p.coff, p.Sk);
-      const int nz = SPLIT ? (kmax + p.kps - 1) / p.kps : 1;
-      if (item < nz) break;
-      item -= nz;
-    }
+    int rb, item, kmax;
+    if (!causal_item<SPLIT>(p, G::ROWS_WG, g, rb, item, kmax)) return;
     blk.rb = rb;
     blk.z = item;
-    const int kmax = causal_kmax(rb, G::ROWS_WG, p.Mp, g, p.coff, p.Sk);
     blk.kbeg = SPLIT ? item * p.kps : 0;
     blk.kend = SPLIT ? min(blk.kbeg + p.kps, kmax) : kmax;
     // the valid keys, up to the diagonal of the block's last row
@@ -1063,17 +1070,10 @@ fwd_ks_kernel(const FwdParams p) {
 
   RowBlock blk;
   if constexpr (CAUSAL) {
-    const int nrb = (p.Mp + ROWS - 1) / ROWS;
-    int item = blockIdx.x, rb = nrb - 1;
-    for (; rb >= 0; --rb) {
-      const int kmax = causal_kmax(rb, ROWS, p.Mp, g, p.coff, p.Sk);
-      const int nz = SPLIT ? (kmax + p.kps - 1) / p.kps : 1;
-      if (item < nz) break;
-      item -= nz;
-    }
+    int rb, item, kmax;
+    if (!causal_item<SPLIT>(p, ROWS, g, rb, item, kmax)) return;
     blk.rb = rb;
     blk.z = item;
-    const int kmax = causal_kmax(rb, ROWS, p.Mp, g, p.coff, p.Sk);
     blk.kbeg = SPLIT ? item * p.kps : 0;
     blk.kend = SPLIT ? min(blk.kbeg + p.kps, kmax) : kmax;
     // the valid keys, up to the diagonal of the block's last row
@@ -1392,11 +1392,7 @@ static hipError_t launch_variant(const FwdParams& p, const LaunchPlan& plan, hip
   const int nrb = (p.Mp + G::ROWS_WG - 1) / G::ROWS_WG;
   dim3 grid;
   if (CAUSAL) {
-    int items = 0;
-    for (int rb = 0; rb < nrb; ++rb) {
-      items += SPLIT ? (causal_kmax(rb, G::ROWS_WG, p.Mp, p.g, p.coff, p.Sk) + p.kps - 1) / p.kps : 1;
-    }
-    grid = dim3(items, p.B * p.Hkv, 1);
+    grid = dim3((unsigned)(nrb * (SPLIT ? std::max(p.zmax, 1) : 1)), p.B * p.Hkv, 1);
   } else {
     grid = dim3(nrb, p.B * p.Hkv, SPLIT ? plan.nsplit : 1);
   }
@@ -1416,11 +1412,7 @@ static hipError_t launch_ks_variant(const FwdParams& p, const LaunchPlan& plan, 
   const int nrb = (p.Mp + ROWS - 1) / ROWS;
   dim3 grid;
   if (CAUSAL) {
-    int items = 0;
-    for (int rb = 0; rb < nrb; ++rb) {
-      items += SPLIT ? (causal_kmax(rb, ROWS, p.Mp, p.g, p.coff, p.Sk) + p.kps - 1) / p.kps : 1;
-    }
-    grid = dim3(items, p.B * p.Hkv, 1);
+    grid = dim3((unsigned)(nrb * (SPLIT ? std::max(p.zmax, 1) : 1)), p.B * p.Hkv, 1);
   } else {
     grid = dim3(nrb, p.B * p.Hkv, SPLIT ? plan.nsplit : 1);
   }
