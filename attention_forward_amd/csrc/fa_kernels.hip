@@ -1316,14 +1316,12 @@ __global__ void __launch_bounds__(256)
 combine_kernel(const FwdParams p) {
   using E = Elem<DTY>;
   constexpr int CPR = D / 4;  // 4-element chunks per row: one per thread
-  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-  const long long per_bh = (long long)p.nrb * ROWS_WG * CPR;
-  const int bh = (int)(i / per_bh);
-  if (bh >= p.B * p.Hkv) return;
-  const int rem = (int)(i - (long long)bh * per_bh);
-  const int rb = rem / (ROWS_WG * CPR);
-  const int rl = (rem / CPR) % ROWS_WG;
-  const int ch = rem % CPR;
+  const int bh = blockIdx.y;  // (batch, kv head); x covers its row blocks
+  const long long rem = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (rem >= (long long)p.nrb * ROWS_WG * CPR) return;
+  const int rb = (int)(rem / (ROWS_WG * CPR));
+  const int rl = (int)((rem / CPR) % ROWS_WG);
+  const int ch = (int)(rem % CPR);
   const int r = rb * ROWS_WG + rl;
   const int g = p.g;
   const int b = udiv(bh, p.Hkv, p.hkv_m), hk = bh - b * p.Hkv;
@@ -1400,8 +1398,8 @@ static hipError_t launch_variant(const FwdParams& p, const LaunchPlan& plan, hip
                      p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !SPLIT) return e;
-  const long long threads = (long long)p.B * p.Hkv * nrb * G::ROWS_WG * (D / 4);
-  hipLaunchKernelGGL((combine_kernel<D, G::ROWS_WG, CAUSAL, DTY, OUTF>), dim3((unsigned)((threads + 255) / 256)),
+  const long long threads = (long long)nrb * G::ROWS_WG * (D / 4);  // per (batch, kv head)
+  hipLaunchKernelGGL((combine_kernel<D, G::ROWS_WG, CAUSAL, DTY, OUTF>), dim3((unsigned)((threads + 255) / 256), p.B * p.Hkv),
                      dim3(256), 0, stream, p);
   return hipGetLastError();
 }
@@ -1419,9 +1417,9 @@ static hipError_t launch_ks_variant(const FwdParams& p, const LaunchPlan& plan, 
   hipLaunchKernelGGL((fwd_ks_kernel<D, QT, KW, BN, CAUSAL, SPLIT, DTY, OUTF>), grid, dim3(KW * 64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !SPLIT) return e;
-  const long long threads = (long long)p.B * p.Hkv * nrb * ROWS * (D / 4);
-  hipLaunchKernelGGL((combine_kernel<D, ROWS, CAUSAL, DTY, OUTF>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
-                     stream, p);
+  const long long threads = (long long)nrb * ROWS * (D / 4);  // per (batch, kv head)
+  hipLaunchKernelGGL((combine_kernel<D, ROWS, CAUSAL, DTY, OUTF>), dim3((unsigned)((threads + 255) / 256), p.B * p.Hkv), dim3(256),
+                     0, stream, p);
   return hipGetLastError();
 }
 
