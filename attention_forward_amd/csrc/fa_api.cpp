@@ -88,7 +88,8 @@ void finish_plan(Plan& pl, int B, int Sq, int Sk, int Hq, int Hkv, int causal) {
 // Default variant for a shape: a function of the shape only (never of the
 // seqused_k values), so equal shapes always run the same kernel.
 //  * Head dim 256: key-split workgroups (32 rows, four waves over the keys),
-//    which read half the LDS bytes per MFMA of the row-split kernel.
+//    which read half the LDS bytes per MFMA of the row-split kernel; 16 rows
+//    when the keys are split as well (below).
 //  * Smaller head dims: row-split workgroups, one wave per 16 packed rows.
 // When the single-pass grid is at most half the compute units, the key
 // range is split into fixed-size ranges, merged afterwards by the
@@ -124,8 +125,22 @@ Plan default_plan(int B, int Sq, int Sk, int Hq, int Hkv, int D, int causal) {
   if (D != 256 && base <= kTargetWorkgroups && Sk >= 128) pl.launch.bn = 128;
   pl.kps = 0;
   if (base <= kTargetWorkgroups / 2) {
-    const int kps = base <= 32 ? 128 : (base <= 64 ? 256 : 512);
-    if (Sk > kps) pl.kps = kps;
+    if (D == 256) {
+      // Split plans at head dim 256 take 16-row key-split workgroups: twice
+      // the workgroups, each with half the rows, for the few rows these
+      // shapes have.  Measured against 32-row workgroups: the 41-row action
+      // expert shape 12.0 -> 10.0 us, a causal 64-row chunk 12.0 -> 11.0 us,
+      // decode 9.5 -> 8.4 us.  The range size follows the 16-row grid.
+      const long long base1 = cdiv(Mp, 16) * BH;
+      const int kps = base1 <= 4 ? 128 : (base1 <= 64 ? 256 : 512);
+      if (Sk > kps) {
+        pl.kps = kps;
+        pl.launch.qt = 1;
+      }
+    } else {
+      const int kps = base <= 32 ? 128 : (base <= 64 ? 256 : 512);
+      if (Sk > kps) pl.kps = kps;
+    }
   }
   finish_plan(pl, B, Sq, Sk, Hq, Hkv, causal);
   return pl;

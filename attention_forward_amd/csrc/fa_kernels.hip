@@ -1464,8 +1464,10 @@ static hipError_t launch_ks_variant(const FwdParams& p, const LaunchPlan& plan, 
   X(kBf16, 64, 2, 4, 64)   \
   X(kBf16, 72, 2, 4, 64)   \
   X(kBf16, 256, 2, 4, 32)  \
+  X(kBf16, 256, 1, 4, 32)  \
   X(kBf16, 256, 2, 2, 32)  \
-  X(kF16, 256, 2, 4, 32)
+  X(kF16, 256, 2, 4, 32)   \
+  X(kF16, 256, 1, 4, 32)
 
 // (nw, kw) of a plan: kw == 1, waves on different rows; kw == nw, every wave
 // on the same rows (key-split kernel); otherwise kw key groups of nw / kw
@@ -1493,7 +1495,8 @@ bool variant_exists(int D, int qt, int nw, int kw, int bn, int nst, int dtype) {
 bool nvfp4_variant_exists(const LaunchPlan& l) {
   return l.dtype == kBf16 && ((l.D == 64 && l.qt == 1 && l.nw == 4 && l.kw == 1 && (l.bn == 64 || l.bn == 128) &&
                                l.nst == 2) ||
-                              (l.D == 256 && l.qt == 2 && l.nw == 4 && l.kw == 4 && l.bn == 32 && l.nst == 1));
+                              (l.D == 256 && (l.qt == 1 || l.qt == 2) && l.nw == 4 && l.kw == 4 && l.bn == 32 &&
+                               l.nst == 1));
 }
 
 template <bool CAUSAL, bool SPLIT>
@@ -1501,7 +1504,8 @@ static hipError_t launch_nvfp4(const FwdParams& p, const LaunchPlan& plan, hipSt
   if (plan.D == 64)
     return plan.bn == 128 ? launch_variant<64, 1, 4, 128, 2, 1, CAUSAL, SPLIT, kBf16, kOutNvfp4>(p, plan, stream)
                           : launch_variant<64, 1, 4, 64, 2, 1, CAUSAL, SPLIT, kBf16, kOutNvfp4>(p, plan, stream);
-  return launch_ks_variant<256, 2, 4, 32, CAUSAL, SPLIT, kBf16, kOutNvfp4>(p, plan, stream);
+  return plan.qt == 1 ? launch_ks_variant<256, 1, 4, 32, CAUSAL, SPLIT, kBf16, kOutNvfp4>(p, plan, stream)
+                      : launch_ks_variant<256, 2, 4, 32, CAUSAL, SPLIT, kBf16, kOutNvfp4>(p, plan, stream);
 }
 
 hipError_t launch_fwd(const FwdParams& p, const LaunchPlan& plan, hipStream_t stream) {

@@ -210,8 +210,11 @@ def test_plan_kernel_choice(lib):
     # ... a padded K/V buffer runs the same plan as the unpadded keys
     assert fa.fa_fwd_plan(1, 1024, 968, 8, 1, 256, 0) == fa.fa_fwd_plan(1, 1024, 1024, 8, 1, 256, 0)
     assert fa.fa_fwd_plan(1, 41, 1009, 8, 1, 256, 0) == fa.fa_fwd_plan(1, 41, 1056, 8, 1, 256, 0)
-    # ... few rows: the keys are split into fixed ranges as well
-    assert fa.fa_fwd_plan(1, 41, 1056, 8, 1, 256, 0) == (2, 4, 4, 32, 1, 128)
+    # ... few rows: the keys are split into fixed ranges as well, over
+    # 16-row workgroups (range size from the 16-row grid: 21 blocks -> 256)
+    assert fa.fa_fwd_plan(1, 41, 1056, 8, 1, 256, 0) == (1, 4, 4, 32, 1, 256)
+    assert fa.fa_fwd_plan(1, 1, 1056, 8, 1, 256, 1) == (1, 4, 4, 32, 1, 128)    # decode: 1 block
+    assert fa.fa_fwd_plan(1, 256, 1024, 8, 1, 256, 1) == (1, 4, 4, 32, 1, 512)  # 128 blocks
     assert fa.fa_fwd_plan(1, 512, 512, 8, 1, 256, 0) == (2, 4, 4, 32, 1, 0)   # 128 blocks: no split
     # Smaller head dims: row-split workgroups, 16 rows per wave
     assert fa.fa_fwd_plan(3, 256, 256, 16, 16, 72, 0) == (1, 4, 1, 128, 2, 0)   # 192 blocks: 128-key tiles
