@@ -76,6 +76,12 @@ CASES = [
     (1, 64, 64, 1, 1, 64, False, None),
     (2, 130, 70, 6, 3, 64, False, [70, 0]),
     (1, 5, 3000, 1, 1, 64, False, None),
+    # long contexts (hundreds of split ranges, 32-bit key offsets up to 64 MiB)
+    # and a large batch of small problems
+    (1, 16, 131072, 8, 1, 256, False, None),
+    (1, 7, 65536, 2, 1, 64, False, [60000]),
+    (2, 33, 40000, 4, 4, 72, True, None),
+    (64, 64, 64, 16, 16, 64, False, None),
 ]
 
 
