@@ -24,6 +24,10 @@ namespace {
 
 constexpr int kMaxDevices = 64;
 constexpr long long kTargetWorkgroups = 256;  // one per compute unit on MI355X
+// Key buffers up to this length take split ranges from the grid size alone,
+// so a padded buffer and its valid keys split identically (bit-identical
+// results); longer buffers size their ranges from the buffer length.
+constexpr int kLongKeys = 2048;
 
 struct Workspace {
   void* ptr = nullptr;
@@ -124,7 +128,21 @@ Plan default_plan(int B, int Sq, int Sk, int Hq, int Hkv, int D, int causal) {
   // which two or three workgroups share a compute unit.
   if (D != 256 && base <= kTargetWorkgroups && Sk >= 128) pl.launch.bn = 128;
   pl.kps = 0;
-  if (base <= kTargetWorkgroups / 2) {
+  if (base <= kTargetWorkgroups / 2 && Sk > kLongKeys) {
+    // Long key buffers: about 32 ranges per row block (fewer when the grid
+    // would exceed one workgroup per compute unit), each a power-of-two
+    // number of keys.  Here the loop dominates, so D256 keeps 32-row
+    // workgroups (half the K/V traffic per MFMA of 16-row ones) unless the
+    // rows fit in 16.  Measured against the short-buffer rule below: 131072
+    // keys, 128 packed rows 242 -> 82 us; decode over 32768 keys 45.8 ->
+    // 19.5 us; 16384 keys, 128 rows 37.7 -> 22.6 us; D64 over 65536 keys
+    // 72.8 -> 23.5 us.
+    const long long splits = std::min(32ll, std::max(2ll, kTargetWorkgroups / base));
+    int kps = 512;
+    while ((long long)kps * splits < Sk) kps *= 2;
+    pl.kps = kps;
+    if (D == 256 && Mp <= 16) pl.launch.qt = 1;
+  } else if (base <= kTargetWorkgroups / 2) {
     if (D == 256) {
       // Split plans at head dim 256 take 16-row key-split workgroups: twice
       // the workgroups, each with half the rows, for the few rows these

@@ -216,6 +216,12 @@ def test_plan_kernel_choice(lib):
     assert fa.fa_fwd_plan(1, 1, 1056, 8, 1, 256, 1) == (1, 4, 4, 32, 1, 128)    # decode: 1 block
     assert fa.fa_fwd_plan(1, 256, 1024, 8, 1, 256, 1) == (1, 4, 4, 32, 1, 512)  # 128 blocks
     assert fa.fa_fwd_plan(1, 512, 512, 8, 1, 256, 0) == (2, 4, 4, 32, 1, 0)   # 128 blocks: no split
+    # ... long key buffers (over 2048 keys): about 32 power-of-two ranges per
+    # row block, 32-row workgroups unless the rows fit in 16
+    assert fa.fa_fwd_plan(1, 16, 131072, 8, 1, 256, 0) == (2, 4, 4, 32, 1, 4096)
+    assert fa.fa_fwd_plan(1, 1, 32768, 8, 1, 256, 1) == (1, 4, 4, 32, 1, 1024)
+    assert fa.fa_fwd_plan(1, 7, 65536, 2, 1, 64, 0) == (1, 4, 1, 128, 2, 2048)
+    assert fa.fa_fwd_plan(1, 256, 8192, 8, 1, 256, 1) == (2, 4, 4, 32, 1, 2048)  # 64 blocks: 4 ranges
     # Smaller head dims: row-split workgroups, 16 rows per wave
     assert fa.fa_fwd_plan(3, 256, 256, 16, 16, 72, 0) == (1, 4, 1, 128, 2, 0)   # 192 blocks: 128-key tiles
     assert fa.fa_fwd_plan(6, 256, 256, 16, 16, 72, 0) == (1, 4, 1, 64, 2, 0)    # 384 blocks: 64-key tiles
