@@ -82,6 +82,9 @@ CASES = [
     (1, 7, 65536, 2, 1, 64, False, [60000]),
     (2, 33, 40000, 4, 4, 72, True, None),
     (64, 64, 64, 16, 16, 64, False, None),
+    # causal decode into long padded caches (split ranges sized from the buffer)
+    (1, 1, 32768, 8, 1, 256, True, [30001]),
+    (2, 3, 20000, 8, 1, 256, True, [19999, 5000]),
 ]
 
 
