@@ -422,7 +422,8 @@ template <class G, int QT>
 __device__ __forceinline__ void pv_tile(f32x4_t (&oacc)[G::DT][QT], const uint32_t (&pk)[G::KVC][QT][4],
                                         const uint8_t* vb) {
   constexpr int NV = G::KVC * G::DT;
-  constexpr int PFV = NV < 4 ? NV : 4;
+  constexpr int PFA = G::WIDE ? 6 : 4;  // reads in flight: measured per head-dim class
+  constexpr int PFV = NV < PFA ? NV : PFA;
   typename G::E::v8 vf[NV];
 #pragma unroll
   for (int i = 0; i < PFV; ++i) vf[i] = load_v<G>(vb, i / G::DT, i % G::DT);
