@@ -1308,17 +1308,18 @@ fwd_ks_kernel(const FwdParams p) {
 }
 
 // Merge of the split-KV partials of one packed row and 4 head-dim elements
-// per thread, in split order (deterministic):
+// per thread (64-thread workgroups: the few rows of a split plan spread over
+// more compute units), in split order (deterministic):
 //   M = max_z m_z over non-empty splits, w_z = l_z 2^(m_z - M),
 //   out = sum_z w_z Ohat_z / sum_z w_z,   lse = ln2 (M + log2 sum_z w_z).
 // The running form below rescales as M grows, which is the same sum.
 template <int D, int ROWS_WG, bool CAUSAL, int DTY, int OUTF>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(64)
 combine_kernel(const FwdParams p) {
   using E = Elem<DTY>;
   constexpr int CPR = D / 4;  // 4-element chunks per row: one per thread
   const int bh = blockIdx.y;  // (batch, kv head); x covers its row blocks
-  const long long rem = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long rem = (long long)blockIdx.x * 64 + threadIdx.x;
   if (rem >= (long long)p.nrb * ROWS_WG * CPR) return;
   const int rb = (int)(rem / (ROWS_WG * CPR));
   const int rl = (int)((rem / CPR) % ROWS_WG);
@@ -1400,8 +1401,8 @@ static hipError_t launch_variant(const FwdParams& p, const LaunchPlan& plan, hip
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !SPLIT) return e;
   const long long threads = (long long)nrb * G::ROWS_WG * (D / 4);  // per (batch, kv head)
-  hipLaunchKernelGGL((combine_kernel<D, G::ROWS_WG, CAUSAL, DTY, OUTF>), dim3((unsigned)((threads + 255) / 256), p.B * p.Hkv),
-                     dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((combine_kernel<D, G::ROWS_WG, CAUSAL, DTY, OUTF>), dim3((unsigned)((threads + 63) / 64), p.B * p.Hkv),
+                     dim3(64), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -1419,7 +1420,7 @@ static hipError_t launch_ks_variant(const FwdParams& p, const LaunchPlan& plan, 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !SPLIT) return e;
   const long long threads = (long long)nrb * ROWS * (D / 4);  // per (batch, kv head)
-  hipLaunchKernelGGL((combine_kernel<D, ROWS, CAUSAL, DTY, OUTF>), dim3((unsigned)((threads + 255) / 256), p.B * p.Hkv), dim3(256),
+  hipLaunchKernelGGL((combine_kernel<D, ROWS, CAUSAL, DTY, OUTF>), dim3((unsigned)((threads + 63) / 64), p.B * p.Hkv), dim3(64),
                      0, stream, p);
   return hipGetLastError();
 }
