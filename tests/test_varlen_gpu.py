@@ -67,6 +67,8 @@ SHAPES = [
     ([130, 17, 300], [200, 17, 64], 8, 1, 256),               # GQA, key-split kernel
     ([41, 20], [1009, 500], 8, 1, 256),                       # few rows, long keys: split-KV path
     ([1, 1, 1, 1], [700, 5, 0, 300], 8, 1, 256),              # decode-like rows
+    ([3, 16], [5000, 2500], 8, 1, 256),                       # long keys: ranges sized from the buffer
+    ([2, 9], [3000, 4100], 4, 2, 64),
 ]
 
 
