@@ -841,13 +841,10 @@ fwd_kernel(const FwdParams p) {
   const int ntiles_all = kend > kbeg ? (kend - kbeg + BN - 1) / BN : 0;
   const int ntiles = ntiles_all > kg ? (ntiles_all - kg + KG - 1) / KG : 0;  // this group's tiles
   const int nsteps = (ntiles_all + KG - 1) / KG;                             // loop trips of every group
-#pragma unroll
-  for (int it = 0; it < NST - 1; ++it)
-    if (it < ntiles) issue(it);
-
   // Q^T fragments (B operand of S^T): lane (col, grp) holds packed row
   // rw0 + 16t + col, head-dim elements 32c + 8grp .. +7 (zero past D).
-  // Loaded after the first K/V copies are on their way.
+  // Loaded before the first K/V copies, whose issue the memory pipeline
+  // paces, so that the Q latency runs under it.
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
     const int r = rw0 + 16 * t + col;
@@ -864,6 +861,10 @@ fwd_kernel(const FwdParams p) {
       qf[t][c] = G::E::cast(x);
     }
   }
+#pragma unroll
+  for (int it = 0; it < NST - 1; ++it)
+    if (it < ntiles) issue(it);
+
   // vmcnt(0) as a builtin, so that the compiler knows the Q fragments have
   // landed; the prologue tiles are waited for along with them.
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
