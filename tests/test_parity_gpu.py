@@ -85,6 +85,13 @@ CASES = [
     # causal decode into long padded caches (split ranges sized from the buffer)
     (1, 1, 32768, 8, 1, 256, True, [30001]),
     (2, 3, 20000, 8, 1, 256, True, [19999, 5000]),
+    # GQA groups larger than a 16-row block: one query position's heads span
+    # several row blocks (and split ranges)
+    (1, 37, 300, 32, 1, 256, False, None),
+    (1, 50, 50, 24, 1, 64, True, None),
+    (2, 3, 777, 48, 2, 256, True, [700, 3]),
+    (1, 129, 129, 20, 1, 72, False, None),
+    (1, 1, 4000, 32, 1, 256, True, [3999]),
 ]
 
 
