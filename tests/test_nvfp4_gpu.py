@@ -104,6 +104,7 @@ CASES = {
     "d64_single_pass": (4, 1024, 1024, 8, 8, 64, False, None),
     "d64_split_gqa": (2, 150, 333, 6, 3, 64, False, [333, 71]),
     "d64_causal": (1, 130, 130, 4, 2, 64, True, None),
+    "d64_large_group": (1, 40, 200, 24, 1, 64, True, [180]),  # a position's heads span two row blocks
 }
 
 

@@ -69,6 +69,7 @@ SHAPES = [
     ([1, 1, 1, 1], [700, 5, 0, 300], 8, 1, 256),              # decode-like rows
     ([3, 16], [5000, 2500], 8, 1, 256),                       # long keys: ranges sized from the buffer
     ([2, 9], [3000, 4100], 4, 2, 64),
+    ([20, 3, 0], [300, 1000, 7], 32, 1, 256),                 # 32 heads per K/V head, a sequence without queries
 ]
 
 
