@@ -133,31 +133,52 @@ Plan default_plan(int B, int Sq, int Sk, int Hq, int Hkv, int D, int causal) {
     // would exceed one workgroup per compute unit), each a power-of-two
     // number of keys.  Here the loop dominates, so D256 keeps 32-row
     // workgroups (half the K/V traffic per MFMA of 16-row ones) unless the
-    // rows fit in 16.  Measured against the short-buffer rule below: 131072
+    // rows fit in 16 or the split grid would still fill under half the
+    // compute units (32 packed rows over 4000 keys: 12.5 -> 10.8 us).  Measured against the short-buffer rule below: 131072
     // keys, 128 packed rows 242 -> 82 us; decode over 32768 keys 45.8 ->
     // 19.5 us; 16384 keys, 128 rows 37.7 -> 22.6 us; D64 over 65536 keys
-    // 72.8 -> 23.5 us.
+    // 72.8 -> 23.5 us.  Ranges of 256 keys rather than 512 where the buffer
+    // allows: D64 decode over 4096 keys 9.2 -> 8.4 us.
     const long long splits = std::min(32ll, std::max(2ll, kTargetWorkgroups / base));
-    int kps = 512;
+    int kps = 256;
     while ((long long)kps * splits < Sk) kps *= 2;
     pl.kps = kps;
-    if (D == 256 && Mp <= 16) pl.launch.qt = 1;
+    if (D == 256 && (Mp <= 16 || base * splits < kTargetWorkgroups / 2)) pl.launch.qt = 1;
   } else if (base <= kTargetWorkgroups / 2) {
     if (D == 256) {
-      // Split plans at head dim 256 take 16-row key-split workgroups: twice
-      // the workgroups, each with half the rows, for the few rows these
-      // shapes have.  Measured against 32-row workgroups: the 41-row action
-      // expert shape 12.0 -> 10.0 us, a causal 64-row chunk 12.0 -> 11.0 us,
-      // decode 9.5 -> 8.4 us.  The range size follows the 16-row grid.
+      // Grids of at most half the compute units at head dim 256 take 16-row
+      // key-split workgroups: twice the workgroups, each with half the rows.
+      // Measured against 32-row workgroups: the 41-row action expert shape
+      // 12.0 -> 10.0 us, a causal 64-row chunk 12.0 -> 11.0 us, decode 9.5 ->
+      // 8.4 us; without a split, 4096 packed rows over 512 keys 11.6 -> 8.8
+      // us.  The range size follows the 16-row grid.
       const long long base1 = cdiv(Mp, 16) * BH;
       const int kps = base1 <= 4 ? 128 : (base1 <= 64 ? 256 : 512);
-      if (Sk > kps) {
-        pl.kps = kps;
-        pl.launch.qt = 1;
-      }
+      if (Sk > kps) pl.kps = kps;
+      pl.launch.qt = 1;
     } else {
       const int kps = base <= 32 ? 128 : (base <= 64 ? 256 : 512);
       if (Sk > kps) pl.kps = kps;
+    }
+  }
+  if (D != 256 && pl.kps == 0) {
+    // Single-pass row-split grids: two key groups of waves on the same rows
+    // (each taking every other 64-key tile, merged in LDS) once a row sees
+    // enough keys, so that two waves share each SIMD.  Long key ranges keep
+    // 64-row blocks (four row waves); grids of at most half the compute
+    // units take 32-row blocks (two row waves), twice the workgroups.
+    // Measured against one group: 16 heads of 1024 x 1024 at D72 13.7 ->
+    // 12.3 us, causal 8 heads of 2048 at D64 20.1 -> 17.7 us, one
+    // 256-token view of 16 heads at D72 5.44 -> 4.96 us.
+    const long long keys = causal ? Sk / 2 : Sk;  // keys per row on average
+    if (base <= kTargetWorkgroups && keys >= 1024) {
+      pl.launch.nw = 8;
+      pl.launch.kw = 2;
+      pl.launch.bn = 64;
+    } else if (base <= kTargetWorkgroups / 2 && keys >= 256) {
+      pl.launch.nw = 4;
+      pl.launch.kw = 2;
+      pl.launch.bn = 64;
     }
   }
   finish_plan(pl, B, Sq, Sk, Hq, Hkv, causal);

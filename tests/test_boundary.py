@@ -215,17 +215,23 @@ def test_plan_kernel_choice(lib):
     assert fa.fa_fwd_plan(1, 41, 1056, 8, 1, 256, 0) == (1, 4, 4, 32, 1, 256)
     assert fa.fa_fwd_plan(1, 1, 1056, 8, 1, 256, 1) == (1, 4, 4, 32, 1, 128)    # decode: 1 block
     assert fa.fa_fwd_plan(1, 256, 1024, 8, 1, 256, 1) == (1, 4, 4, 32, 1, 512)  # 128 blocks
-    assert fa.fa_fwd_plan(1, 512, 512, 8, 1, 256, 0) == (2, 4, 4, 32, 1, 0)   # 128 blocks: no split
+    assert fa.fa_fwd_plan(1, 512, 512, 8, 1, 256, 0) == (1, 4, 4, 32, 1, 0)   # 128 blocks: 16-row blocks, no split
     # ... long key buffers (over 2048 keys): about 32 power-of-two ranges per
     # row block, 32-row workgroups unless the rows fit in 16
     assert fa.fa_fwd_plan(1, 16, 131072, 8, 1, 256, 0) == (2, 4, 4, 32, 1, 4096)
     assert fa.fa_fwd_plan(1, 1, 32768, 8, 1, 256, 1) == (1, 4, 4, 32, 1, 1024)
     assert fa.fa_fwd_plan(1, 7, 65536, 2, 1, 64, 0) == (1, 4, 1, 128, 2, 2048)
     assert fa.fa_fwd_plan(1, 256, 8192, 8, 1, 256, 1) == (2, 4, 4, 32, 1, 2048)  # 64 blocks: 4 ranges
+    assert fa.fa_fwd_plan(1, 1, 4096, 8, 8, 64, 1) == (1, 4, 1, 128, 2, 256)     # ranges of at least 256 keys
     # Smaller head dims: row-split workgroups, 16 rows per wave
     assert fa.fa_fwd_plan(3, 256, 256, 16, 16, 72, 0) == (1, 4, 1, 128, 2, 0)   # 192 blocks: 128-key tiles
     assert fa.fa_fwd_plan(6, 256, 256, 16, 16, 72, 0) == (1, 4, 1, 64, 2, 0)    # 384 blocks: 64-key tiles
     assert fa.fa_fwd_plan(2, 77, 77, 16, 16, 72, 1) == (1, 4, 1, 64, 2, 0)      # fewer than 128 keys
+    # ... two key groups on the same rows once a row sees enough keys
+    assert fa.fa_fwd_plan(1, 256, 256, 16, 16, 72, 0) == (1, 4, 2, 64, 2, 0)    # 64 blocks: 32-row blocks
+    assert fa.fa_fwd_plan(1, 1024, 1024, 16, 16, 72, 0) == (1, 8, 2, 64, 2, 0)  # 1024 keys per row
+    assert fa.fa_fwd_plan(1, 2048, 2048, 8, 8, 64, 1) == (1, 8, 2, 64, 2, 0)    # causal: 1024 on average
+    assert fa.fa_fwd_plan(4, 512, 512, 8, 8, 64, 0) == (1, 4, 1, 128, 2, 0)     # 512 keys, 256 blocks: one group
     assert fa.fa_fwd_plan(1, 64, 64, 1, 1, 64, 0) == (1, 4, 1, 64, 2, 0)
 
 

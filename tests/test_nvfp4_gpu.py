@@ -105,6 +105,8 @@ CASES = {
     "d64_split_gqa": (2, 150, 333, 6, 3, 64, False, [333, 71]),
     "d64_causal": (1, 130, 130, 4, 2, 64, True, None),
     "d64_large_group": (1, 40, 200, 24, 1, 64, True, [180]),  # a position's heads span two row blocks
+    "d64_key_groups": (1, 1024, 1024, 12, 12, 64, False, None),  # two key groups of four row waves
+    "d64_key_groups_32row": (1, 256, 256, 16, 16, 64, False, None),  # two key groups of two row waves
 }
 
 

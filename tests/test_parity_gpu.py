@@ -92,6 +92,12 @@ CASES = [
     (2, 3, 777, 48, 2, 256, True, [700, 3]),
     (1, 129, 129, 20, 1, 72, False, None),
     (1, 1, 4000, 32, 1, 256, True, [3999]),
+    # default plans with two key groups of waves (row-split) and 16-row
+    # key-split blocks without a split
+    (1, 256, 256, 16, 16, 72, False, None),
+    (1, 1024, 1024, 12, 12, 72, False, [1000]),
+    (1, 2048, 2048, 5, 5, 64, True, None),
+    (1, 512, 512, 8, 1, 256, False, [500]),
 ]
 
 

@@ -23,7 +23,7 @@ VARIANTS = [(64, 1, 4, 1, 64, 2), (64, 1, 4, 1, 128, 2), (72, 1, 4, 1, 128, 2), 
             (72, 1, 4, 1, 64, 2), (72, 1, 4, 1, 64, 3), (72, 1, 4, 1, 64, 4), (72, 2, 2, 1, 64, 2), (72, 2, 2, 1, 64, 3), (72, 2, 4, 1, 64, 2), (256, 1, 4, 1, 32, 2), (256, 1, 4, 1, 32, 4), (256, 1, 4, 1, 64, 2),
             (256, 2, 4, 1, 32, 2), (256, 2, 4, 1, 32, 4), (256, 2, 4, 1, 64, 2),
             (64, 2, 4, 4, 64, 1), (72, 2, 4, 4, 64, 1), (256, 2, 4, 4, 32, 1), (256, 1, 4, 4, 32, 1), (256, 2, 2, 2, 32, 1),
-            (64, 1, 8, 2, 64, 2), (72, 1, 8, 2, 64, 2), (72, 1, 4, 2, 64, 2)]
+            (64, 1, 8, 2, 64, 2), (72, 1, 8, 2, 64, 2), (72, 1, 4, 2, 64, 2), (64, 1, 4, 2, 64, 2)]
 
 SHAPES = {
     # D: (non-causal: B, Sq, Sk, Hq, Hkv, n_valid), (causal: B, S, Hq, Hkv)

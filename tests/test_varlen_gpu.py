@@ -70,6 +70,8 @@ SHAPES = [
     ([3, 16], [5000, 2500], 8, 1, 256),                       # long keys: ranges sized from the buffer
     ([2, 9], [3000, 4100], 4, 2, 64),
     ([20, 3, 0], [300, 1000, 7], 32, 1, 256),                 # 32 heads per K/V head, a sequence without queries
+    ([1024], [1024], 12, 12, 72),                             # two key groups of four row waves
+    ([256, 100], [256, 200], 16, 16, 64),                     # two key groups of two row waves
 ]
 
 
