@@ -24,6 +24,7 @@ namespace {
 
 constexpr int kMaxDevices = 64;
 constexpr long long kTargetWorkgroups = 256;  // one per compute unit on MI355X
+constexpr int kLongTiles = 1024;              // keys from which row-split grids of any size take 128-key tiles
 // Key buffers up to this length take split ranges from the grid size alone,
 // so a padded buffer and its valid keys split identically (bit-identical
 // results); longer buffers size their ranges from the buffer length.
@@ -125,8 +126,10 @@ Plan default_plan(int B, int Sq, int Sk, int Hq, int Hkv, int D, int causal) {
   // per key) when the single-pass grid fits the compute units in one round
   // and the buffer holds at least one such tile.  Their 96 KB of stages allow
   // one workgroup per compute unit, so larger grids keep 64-key tiles, with
-  // which two or three workgroups share a compute unit.
-  if (D != 256 && base <= kTargetWorkgroups && Sk >= 128) pl.launch.bn = 128;
+  // which two or three workgroups share a compute unit, unless the rows see
+  // at least kLongTiles keys (two rounds of 1024 x 1024 at D64, 16 heads:
+  // 18.2 -> 15.3 us; causal 4096 x 4096, 8 heads: 53.2 -> 48.7 us).
+  if (D != 256 && ((base <= kTargetWorkgroups && Sk >= 128) || Sk >= kLongTiles)) pl.launch.bn = 128;
   pl.kps = 0;
   if (base <= kTargetWorkgroups / 2 && Sk > kLongKeys) {
     // Long key buffers: about 32 ranges per row block (fewer when the grid
@@ -168,10 +171,11 @@ Plan default_plan(int B, int Sq, int Sk, int Hq, int Hkv, int D, int causal) {
     // 64-row blocks (four row waves); grids of at most half the compute
     // units take 32-row blocks (two row waves), twice the workgroups.
     // Measured against one group: 16 heads of 1024 x 1024 at D72 13.7 ->
-    // 12.3 us, causal 8 heads of 2048 at D64 20.1 -> 17.7 us, one
+    // 12.3 us, 768 x 768 at D72 11.0 -> 10.0 us, causal 1024 x 1024 at D72
+    // 14.7 -> 12.8 us, causal 8 heads of 2048 at D64 20.1 -> 17.7 us, one
     // 256-token view of 16 heads at D72 5.44 -> 4.96 us.
     const long long keys = causal ? Sk / 2 : Sk;  // keys per row on average
-    if (base <= kTargetWorkgroups && keys >= 1024) {
+    if (base <= kTargetWorkgroups && Sk >= 768) {
       pl.launch.nw = 8;
       pl.launch.kw = 2;
       pl.launch.bn = 64;

@@ -98,6 +98,8 @@ CASES = [
     (1, 1024, 1024, 12, 12, 72, False, [1000]),
     (1, 2048, 2048, 5, 5, 64, True, None),
     (1, 512, 512, 8, 1, 256, False, [500]),
+    (1, 1024, 1024, 16, 16, 72, True, None),      # causal, two key groups
+    (2, 1024, 1024, 16, 16, 64, False, None),     # two rounds of 128-key tiles
 ]
 
 
