@@ -24,7 +24,6 @@ namespace {
 
 constexpr int kMaxDevices = 64;
 constexpr long long kTargetWorkgroups = 256;  // one per compute unit on MI355X
-constexpr int kLongTiles = 1024;              // keys from which row-split grids of any size take 128-key tiles
 // Key buffers up to this length take split ranges from the grid size alone,
 // so a padded buffer and its valid keys split identically (bit-identical
 // results); longer buffers size their ranges from the buffer length.
@@ -126,10 +125,8 @@ Plan default_plan(int B, int Sq, int Sk, int Hq, int Hkv, int D, int causal) {
   // per key) when the single-pass grid fits the compute units in one round
   // and the buffer holds at least one such tile.  Their 96 KB of stages allow
   // one workgroup per compute unit, so larger grids keep 64-key tiles, with
-  // which two or three workgroups share a compute unit, unless the rows see
-  // at least kLongTiles keys (two rounds of 1024 x 1024 at D64, 16 heads:
-  // 18.2 -> 15.3 us; causal 4096 x 4096, 8 heads: 53.2 -> 48.7 us).
-  if (D != 256 && ((base <= kTargetWorkgroups && Sk >= 128) || Sk >= kLongTiles)) pl.launch.bn = 128;
+  // which two or three workgroups share a compute unit.
+  if (D != 256 && base <= kTargetWorkgroups && Sk >= 128) pl.launch.bn = 128;
   pl.kps = 0;
   if (base <= kTargetWorkgroups / 2 && Sk > kLongKeys) {
     // Long key buffers: about 32 ranges per row block (fewer when the grid
@@ -183,6 +180,20 @@ Plan default_plan(int B, int Sq, int Sk, int Hq, int Hkv, int D, int causal) {
       pl.launch.nw = 4;
       pl.launch.kw = 2;
       pl.launch.bn = 64;
+    } else if (!causal && base >= 4 * kTargetWorkgroups && Sk >= 1024) {
+      // Four or more rounds of 64-row blocks over long key ranges: 32 rows
+      // per wave (128-row blocks) halve the LDS reads per row.  Measured
+      // against 16 rows per wave: 1024 blocks of 2048 x 2048 at D72 93 ->
+      // 56 us (128-key tiles) and 32/8 GQA heads at D64 53.4 -> 45.4 us;
+      // 2048 blocks of 1024 keys at D64 56.7 -> 46.6 us.  At 512 blocks and
+      // for causal grids one 16-row wave per SIMD stays ahead.
+      pl.launch.qt = 2;
+    } else if (D == 64 && base > kTargetWorkgroups && base < 4 * kTargetWorkgroups && Sk >= 1024) {
+      // Two or three rounds at D64 over long key ranges: 128-key tiles (two
+      // rounds of 1024 x 1024, 16 heads: 18.2 -> 15.3 us; causal 4096 x
+      // 4096, 8 heads: 53.2 -> 48.7 us).  At D72 the larger stages cost more
+      // than they save (4 x 1024 x 1024, 8 heads: 20.6 -> 27.2 us).
+      pl.launch.bn = 128;
     }
   }
   finish_plan(pl, B, Sq, Sk, Hq, Hkv, causal);

@@ -1466,7 +1466,9 @@ static hipError_t launch_ks_variant(const FwdParams& p, const LaunchPlan& plan, 
   X(kF16, 64, 1, 4, 2, 64, 2)    \
   X(kF16, 64, 1, 2, 2, 64, 2)    \
   X(kF16, 72, 1, 4, 2, 64, 2)    \
-  X(kF16, 72, 1, 2, 2, 64, 2)
+  X(kF16, 72, 1, 2, 2, 64, 2)    \
+  X(kF16, 64, 2, 4, 1, 64, 2)    \
+  X(kF16, 72, 2, 4, 1, 64, 2)
 
 #define FA_KS_VARIANTS(X)  \
   X(kBf16, 64, 2, 4, 64)   \
@@ -1505,12 +1507,15 @@ bool nvfp4_variant_exists(const LaunchPlan& l) {
                                l.nst == 2) ||
                               (l.D == 64 && l.qt == 1 && (l.nw == 4 || l.nw == 8) && l.kw == 2 && l.bn == 64 &&
                                l.nst == 2) ||
+                              (l.D == 64 && l.qt == 2 && l.nw == 4 && l.kw == 1 && l.bn == 64 && l.nst == 2) ||
                               (l.D == 256 && (l.qt == 1 || l.qt == 2) && l.nw == 4 && l.kw == 4 && l.bn == 32 &&
                                l.nst == 1));
 }
 
 template <bool CAUSAL, bool SPLIT>
 static hipError_t launch_nvfp4(const FwdParams& p, const LaunchPlan& plan, hipStream_t stream) {
+  if (plan.D == 64 && plan.qt == 2)
+    return launch_variant<64, 2, 4, 64, 2, 1, CAUSAL, SPLIT, kBf16, kOutNvfp4>(p, plan, stream);
   if (plan.D == 64 && plan.kw == 2)
     return plan.nw == 8 ? launch_variant<64, 1, 4, 64, 2, 2, CAUSAL, SPLIT, kBf16, kOutNvfp4>(p, plan, stream)
                         : launch_variant<64, 1, 2, 64, 2, 2, CAUSAL, SPLIT, kBf16, kOutNvfp4>(p, plan, stream);

@@ -234,6 +234,9 @@ def test_plan_kernel_choice(lib):
     assert fa.fa_fwd_plan(4, 512, 512, 8, 8, 64, 0) == (1, 4, 1, 128, 2, 0)     # 512 keys, 256 blocks: one group
     assert fa.fa_fwd_plan(1, 1024, 1024, 16, 16, 72, 1) == (1, 8, 2, 64, 2, 0)  # causal over 1024 keys
     assert fa.fa_fwd_plan(2, 1024, 1024, 16, 16, 64, 0) == (1, 4, 1, 128, 2, 0) # 512 blocks, 1024 keys: 128-key tiles
+    assert fa.fa_fwd_plan(4, 1024, 1024, 8, 8, 72, 0) == (1, 4, 1, 64, 2, 0)    # ... not at D72
+    assert fa.fa_fwd_plan(8, 1024, 1024, 16, 16, 64, 0) == (2, 4, 1, 64, 2, 0)  # 2048 blocks: 32 rows per wave
+    assert fa.fa_fwd_plan(1, 2048, 2048, 32, 4, 64, 1) == (1, 4, 1, 64, 2, 0)   # causal: 16 rows per wave
     assert fa.fa_fwd_plan(1, 64, 64, 1, 1, 64, 0) == (1, 4, 1, 64, 2, 0)
 
 

@@ -100,6 +100,8 @@ CASES = [
     (1, 512, 512, 8, 1, 256, False, [500]),
     (1, 1024, 1024, 16, 16, 72, True, None),      # causal, two key groups
     (2, 1024, 1024, 16, 16, 64, False, None),     # two rounds of 128-key tiles
+    (4, 1024, 1024, 16, 16, 64, False, None),     # 32 rows per wave, 128-row blocks
+    (2, 2048, 2048, 16, 16, 72, False, [2048, 1500]),
 ]
 
 

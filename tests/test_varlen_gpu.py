@@ -72,6 +72,7 @@ SHAPES = [
     ([20, 3, 0], [300, 1000, 7], 32, 1, 256),                 # 32 heads per K/V head, a sequence without queries
     ([1024], [1024], 12, 12, 72),                             # two key groups of four row waves
     ([256, 100], [256, 200], 16, 16, 64),                     # two key groups of two row waves
+    ([1024, 1024, 1000, 1024], [1024, 1024, 1024, 900], 16, 16, 64),  # 32 rows per wave
 ]
 
 
