@@ -108,6 +108,7 @@ CASES = {
     "d64_key_groups": (1, 1024, 1024, 12, 12, 64, False, None),  # two key groups of four row waves
     "d64_key_groups_32row": (1, 256, 256, 16, 16, 64, False, None),  # two key groups of two row waves
     "d64_32_rows_per_wave": (4, 1024, 1024, 16, 16, 64, False, None),
+    "d256_16row_single_pass": (1, 512, 512, 8, 1, 256, False, [480]),
 }
 
 
