@@ -152,14 +152,27 @@ Plan default_plan(int B, int Sq, int Sk, int Hq, int Hkv, int D, int causal) {
       // 12.0 -> 10.0 us, a causal 64-row chunk 12.0 -> 11.0 us, decode 9.5 ->
       // 8.4 us; without a split, 4096 packed rows over 512 keys 11.6 -> 8.8
       // us.  The range size follows the 16-row grid.
+      // A 16-row grid of more than half the compute units is not split
+      // further (8 x 41 rows over 1056 keys: 24.8 -> 16.5 us).
       const long long base1 = cdiv(Mp, 16) * BH;
       const int kps = base1 <= 4 ? 128 : (base1 <= 64 ? 256 : 512);
-      if (Sk > kps) pl.kps = kps;
+      if (Sk > kps && base1 <= kTargetWorkgroups / 2) pl.kps = kps;
       pl.launch.qt = 1;
     } else {
       const int kps = base <= 32 ? 128 : (base <= 64 ? 256 : 512);
       if (Sk > kps) pl.kps = kps;
     }
+  }
+  if (D == 256 && !causal && pl.kps == 0 && base >= 4 * kTargetWorkgroups) {
+    // Four or more rounds of 32-row key-split blocks: every compute unit
+    // would pull the whole K/V of its head from L2 per 32 rows.  Row-split
+    // blocks of four 32-row waves share each K/V tile among 128 rows
+    // (4 x 1024 x 1024 prefix rows, 8/1 heads: 65.1 -> 46.3 us).
+    pl.launch.qt = 2;
+    pl.launch.nw = 4;
+    pl.launch.kw = 1;
+    pl.launch.bn = 32;
+    pl.launch.nst = 2;
   }
   if (D != 256 && pl.kps == 0) {
     // Single-pass row-split grids: two key groups of waves on the same rows

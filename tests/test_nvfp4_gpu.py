@@ -109,6 +109,7 @@ CASES = {
     "d64_key_groups_32row": (1, 256, 256, 16, 16, 64, False, None),  # two key groups of two row waves
     "d64_32_rows_per_wave": (4, 1024, 1024, 16, 16, 64, False, None),
     "d256_16row_single_pass": (1, 512, 512, 8, 1, 256, False, [480]),
+    "d256_row_split_batched": (4, 1024, 1024, 8, 1, 256, False, [968, 1024, 300, 5]),
 }
 
 

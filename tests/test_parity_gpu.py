@@ -102,6 +102,8 @@ CASES = [
     (2, 1024, 1024, 16, 16, 64, False, None),     # two rounds of 128-key tiles
     (4, 1024, 1024, 16, 16, 64, False, None),     # 32 rows per wave, 128-row blocks
     (2, 2048, 2048, 16, 16, 72, False, [2048, 1500]),
+    (8, 41, 1056, 8, 1, 256, False, [1009, 1, 0, 1056, 500, 41, 1008, 7]),   # batched action expert, no split
+    (4, 1024, 1024, 8, 1, 256, False, [968, 1024, 300, 5]),                 # batched prefix: row-split D256
 ]
 
 

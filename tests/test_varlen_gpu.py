@@ -73,6 +73,7 @@ SHAPES = [
     ([1024], [1024], 12, 12, 72),                             # two key groups of four row waves
     ([256, 100], [256, 200], 16, 16, 64),                     # two key groups of two row waves
     ([1024, 1024, 1000, 1024], [1024, 1024, 1024, 900], 16, 16, 64),  # 32 rows per wave
+    ([1024, 1000, 1024, 1024], [968, 1024, 1024, 1024], 8, 1, 256),   # D256 row-split, 128 rows
 ]
 
 
