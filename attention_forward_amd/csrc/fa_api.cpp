@@ -173,6 +173,15 @@ Plan default_plan(int B, int Sq, int Sk, int Hq, int Hkv, int D, int causal) {
     pl.launch.kw = 1;
     pl.launch.bn = 32;
     pl.launch.nst = 2;
+  } else if (D == 256 && !causal && pl.kps == 0 && base > kTargetWorkgroups) {
+    // Two or three rounds: row-split blocks of four 16-row waves over 64-key
+    // tiles (2 x 768 x 768 prefix rows: 27.5 -> 25.6 us; 2 x 1024 x 1024:
+    // 34.5 -> 32.8 us).
+    pl.launch.qt = 1;
+    pl.launch.nw = 4;
+    pl.launch.kw = 1;
+    pl.launch.bn = 64;
+    pl.launch.nst = 2;
   }
   if (D != 256 && pl.kps == 0) {
     // Single-pass row-split grids: two key groups of waves on the same rows

@@ -1469,7 +1469,8 @@ static hipError_t launch_ks_variant(const FwdParams& p, const LaunchPlan& plan, 
   X(kF16, 72, 1, 2, 2, 64, 2)    \
   X(kF16, 64, 2, 4, 1, 64, 2)    \
   X(kF16, 72, 2, 4, 1, 64, 2)    \
-  X(kF16, 256, 2, 4, 1, 32, 2)
+  X(kF16, 256, 2, 4, 1, 32, 2)   \
+  X(kF16, 256, 1, 4, 1, 64, 2)
 
 #define FA_KS_VARIANTS(X)  \
   X(kBf16, 64, 2, 4, 64)   \
@@ -1510,6 +1511,7 @@ bool nvfp4_variant_exists(const LaunchPlan& l) {
                                l.nst == 2) ||
                               (l.D == 64 && l.qt == 2 && l.nw == 4 && l.kw == 1 && l.bn == 64 && l.nst == 2) ||
                               (l.D == 256 && l.qt == 2 && l.nw == 4 && l.kw == 1 && l.bn == 32 && l.nst == 2) ||
+                              (l.D == 256 && l.qt == 1 && l.nw == 4 && l.kw == 1 && l.bn == 64 && l.nst == 2) ||
                               (l.D == 256 && (l.qt == 1 || l.qt == 2) && l.nw == 4 && l.kw == 4 && l.bn == 32 &&
                                l.nst == 1));
 }
@@ -1517,7 +1519,8 @@ bool nvfp4_variant_exists(const LaunchPlan& l) {
 template <bool CAUSAL, bool SPLIT>
 static hipError_t launch_nvfp4(const FwdParams& p, const LaunchPlan& plan, hipStream_t stream) {
   if (plan.D == 256 && plan.kw == 1)
-    return launch_variant<256, 2, 4, 32, 2, 1, CAUSAL, SPLIT, kBf16, kOutNvfp4>(p, plan, stream);
+    return plan.qt == 2 ? launch_variant<256, 2, 4, 32, 2, 1, CAUSAL, SPLIT, kBf16, kOutNvfp4>(p, plan, stream)
+                        : launch_variant<256, 1, 4, 64, 2, 1, CAUSAL, SPLIT, kBf16, kOutNvfp4>(p, plan, stream);
   if (plan.D == 64 && plan.qt == 2)
     return launch_variant<64, 2, 4, 64, 2, 1, CAUSAL, SPLIT, kBf16, kOutNvfp4>(p, plan, stream);
   if (plan.D == 64 && plan.kw == 2)

@@ -218,6 +218,7 @@ def test_plan_kernel_choice(lib):
     assert fa.fa_fwd_plan(1, 512, 512, 8, 1, 256, 0) == (1, 4, 4, 32, 1, 0)   # 128 blocks: 16-row blocks, no split
     assert fa.fa_fwd_plan(8, 41, 1056, 8, 1, 256, 0) == (1, 4, 4, 32, 1, 0)   # 168 16-row blocks: no split
     assert fa.fa_fwd_plan(4, 1024, 1024, 8, 1, 256, 0) == (2, 4, 1, 32, 2, 0)  # 1024 blocks: row-split, 128 rows
+    assert fa.fa_fwd_plan(2, 1024, 1024, 8, 1, 256, 0) == (1, 4, 1, 64, 2, 0)  # 512 blocks: row-split, 64 rows
     assert fa.fa_fwd_plan(2, 2048, 2048, 8, 1, 256, 1) == (2, 4, 4, 32, 1, 0)  # causal keeps key-split
     # ... long key buffers (over 2048 keys): about 32 power-of-two ranges per
     # row block, 32-row workgroups unless the rows fit in 16

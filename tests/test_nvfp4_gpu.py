@@ -110,6 +110,7 @@ CASES = {
     "d64_32_rows_per_wave": (4, 1024, 1024, 16, 16, 64, False, None),
     "d256_16row_single_pass": (1, 512, 512, 8, 1, 256, False, [480]),
     "d256_row_split_batched": (4, 1024, 1024, 8, 1, 256, False, [968, 1024, 300, 5]),
+    "d256_row_split_64_rows": (2, 768, 768, 8, 1, 256, False, [700, 768]),
 }
 
 

@@ -104,6 +104,7 @@ CASES = [
     (2, 2048, 2048, 16, 16, 72, False, [2048, 1500]),
     (8, 41, 1056, 8, 1, 256, False, [1009, 1, 0, 1056, 500, 41, 1008, 7]),   # batched action expert, no split
     (4, 1024, 1024, 8, 1, 256, False, [968, 1024, 300, 5]),                 # batched prefix: row-split D256
+    (2, 768, 768, 8, 1, 256, False, [700, 768]),                            # row-split D256, 64-key tiles
 ]
 
 
