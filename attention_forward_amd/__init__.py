@@ -25,6 +25,7 @@ from .fa import (  # noqa: F401
     fa_set_workspace,
     fa_status_string,
     load_library,
+    reserve_workspace,
 )
 
 __all__ = [
@@ -47,4 +48,5 @@ __all__ = [
     "fa_set_workspace",
     "fa_status_string",
     "load_library",
+    "reserve_workspace",
 ]

@@ -254,10 +254,14 @@ int check_args(const void* q, const void* k, const void* v, void* out, float* ls
     return FA_ERR_ALIGN;
   const size_t qb = (size_t)B * Sq * Hq * D * 2, kb = (size_t)B * Sk * Hkv * D * 2;
   if (overlap(out, qb, q, qb) || overlap(out, qb, k, kb) || overlap(out, qb, v, kb)) return FA_ERR_ALIAS;
+  // seqused_k is read by workgroups that may start after others have
+  // written their output rows, so it may not share a byte with out or lse.
+  const size_t sb = (size_t)B * sizeof(int32_t);
+  if (seqused_k != nullptr && overlap(out, qb, seqused_k, sb)) return FA_ERR_ALIAS;
   if (lse != nullptr) {
     const size_t lb = (size_t)B * Hq * Sq * sizeof(float);
     if (overlap(lse, lb, q, qb) || overlap(lse, lb, k, kb) || overlap(lse, lb, v, kb) ||
-        overlap(lse, lb, out, qb))
+        overlap(lse, lb, out, qb) || (seqused_k != nullptr && overlap(lse, lb, seqused_k, sb)))
       return FA_ERR_ALIAS;
   }
   return FA_OK;
@@ -322,10 +326,12 @@ int check_strided(const void* q, const void* k, const void* v, void* out, float*
   view_span(out, B, Sq, Hq, D, vo, o0, o1);
   if (spans_overlap(o0, o1, q0, q1) || spans_overlap(o0, o1, k0, k1) || spans_overlap(o0, o1, v0, v1))
     return FA_ERR_ALIAS;
+  const uintptr_t s0 = (uintptr_t)seqused_k, s1 = s0 + (uintptr_t)B * sizeof(int32_t);
+  if (seqused_k != nullptr && spans_overlap(o0, o1, s0, s1)) return FA_ERR_ALIAS;
   if (lse != nullptr) {
     const uintptr_t l0 = (uintptr_t)lse, l1 = l0 + (uintptr_t)B * Hq * Sq * sizeof(float);
     if (spans_overlap(l0, l1, q0, q1) || spans_overlap(l0, l1, k0, k1) || spans_overlap(l0, l1, v0, v1) ||
-        spans_overlap(l0, l1, o0, o1))
+        spans_overlap(l0, l1, o0, o1) || (seqused_k != nullptr && spans_overlap(l0, l1, s0, s1)))
       return FA_ERR_ALIAS;
   }
   return FA_OK;
@@ -434,7 +440,7 @@ const char* fa_status_string(int code) {
     case FA_ERR_SCALE: return "FA_ERR_SCALE: scale must be finite and > 0";
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: split-KV path needs a registered workspace of fa_fwd_workspace_bytes() bytes";
     case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: the HIP runtime reported an error";
-    case FA_ERR_ALIAS: return "FA_ERR_ALIAS: out or lse overlaps an input";
+    case FA_ERR_ALIAS: return "FA_ERR_ALIAS: out or lse overlaps an input (q, k, v, seqused_k, cu_seqlens) or each other";
     default: return "FA_ERR_UNKNOWN: unknown status code";
   }
 }
@@ -506,10 +512,14 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* out, float*
   if ((lse != nullptr && !aligned(lse, 4)) || !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4))
     return FA_ERR_ALIGN;
   const size_t qb = (size_t)total_q * Hq * D * 2, kb = (size_t)total_k * Hkv * D * 2;
-  if (overlap(out, qb, q, qb) || overlap(out, qb, k, kb) || overlap(out, qb, v, kb)) return FA_ERR_ALIAS;
+  const size_t cb = (size_t)(B + 1) * sizeof(int32_t);
+  if (overlap(out, qb, q, qb) || overlap(out, qb, k, kb) || overlap(out, qb, v, kb) ||
+      overlap(out, qb, cu_seqlens_q, cb) || overlap(out, qb, cu_seqlens_k, cb))
+    return FA_ERR_ALIAS;
   if (lse != nullptr) {
     const size_t lb = (size_t)Hq * total_q * sizeof(float);
-    if (overlap(lse, lb, q, qb) || overlap(lse, lb, k, kb) || overlap(lse, lb, v, kb) || overlap(lse, lb, out, qb))
+    if (overlap(lse, lb, q, qb) || overlap(lse, lb, k, kb) || overlap(lse, lb, v, kb) || overlap(lse, lb, out, qb) ||
+        overlap(lse, lb, cu_seqlens_q, cb) || overlap(lse, lb, cu_seqlens_k, cb))
       return FA_ERR_ALIAS;
   }
   Plan pl = default_plan(B, max_seqlen_q, max_seqlen_k, Hq, Hkv, D, causal);
@@ -538,14 +548,18 @@ int fa_fwd_nvfp4(const void* q, const void* k, const void* v, void* out_fp4, voi
   if ((lse != nullptr && !aligned(lse, 4)) || (seqused_k != nullptr && !aligned(seqused_k, 4))) return FA_ERR_ALIGN;
   const size_t rows = (size_t)B * Sq * Hq;
   const size_t qb = rows * D * 2, kb = (size_t)B * Sk * Hkv * D * 2, cb = rows * D / 2, sb = rows * D / 16;
+  const size_t ub = (size_t)B * sizeof(int32_t);
   if (overlap(out_fp4, cb, q, qb) || overlap(out_fp4, cb, k, kb) || overlap(out_fp4, cb, v, kb) ||
       overlap(out_sf, sb, q, qb) || overlap(out_sf, sb, k, kb) || overlap(out_sf, sb, v, kb) ||
       overlap(out_fp4, cb, out_sf, sb))
     return FA_ERR_ALIAS;
+  if (seqused_k != nullptr && (overlap(out_fp4, cb, seqused_k, ub) || overlap(out_sf, sb, seqused_k, ub)))
+    return FA_ERR_ALIAS;
   if (lse != nullptr) {
     const size_t lb = rows * sizeof(float);
     if (overlap(lse, lb, q, qb) || overlap(lse, lb, k, kb) || overlap(lse, lb, v, kb) ||
-        overlap(lse, lb, out_fp4, cb) || overlap(lse, lb, out_sf, sb))
+        overlap(lse, lb, out_fp4, cb) || overlap(lse, lb, out_sf, sb) ||
+        (seqused_k != nullptr && overlap(lse, lb, seqused_k, ub)))
       return FA_ERR_ALIAS;
   }
   Plan pl = default_plan(B, Sq, Sk, Hq, Hkv, D, causal);

@@ -4,10 +4,11 @@ The functions ``fa_fwd``, ``fa_fwd_workspace_bytes``, ``fa_set_workspace``,
 ``fa_status_string`` and ``fa_abi_version`` mirror the C entry points one to
 one and take plain integers for device pointers and streams.  ``attention``
 is the tensor-level convenience on top: it checks the torch tensors, takes
-the current HIP stream, registers a split-KV workspace when the shape needs
-one, allocates ``out``/``lse`` only when they are not passed (the
-allocation-free form is the one with both passed), and raises on any error
-code.  Every arithmetic step runs in the HIP kernels; there is no other
+the current HIP stream, registers that stream's split-KV workspace when the
+shape needs one (reserved once per stream, never released, never grown
+during graph capture), allocates ``out``/``lse`` only when they are not
+passed (the allocation-free form is the one with both passed), and raises
+on any error code.  Every arithmetic step runs in the HIP kernels; there is no other
 implementation to fall back to.
 """
 
@@ -165,25 +166,87 @@ def fa_abi_version() -> int:
 
 # ------------------------------------------------------------- tensor interface
 
-_workspaces = {}  # device index -> registered torch buffer
+# Split-KV workspaces: one torch buffer per (device index, stream handle),
+# so calls queued on different streams never share partial results.  A
+# buffer that has ever been registered is never released: a HIP graph
+# captured earlier keeps its address in the kernel arguments and writes
+# there on every replay, so a superseded buffer moves to _retired and lives
+# as long as the process.  Registration and the call that uses it happen
+# under one lock, because the library keeps one registered workspace per
+# device and reads it when the call is queued.
+_ws_lock = threading.RLock()
+_workspaces = {}  # (device index, stream handle) -> torch uint8 buffer
+_retired = []     # superseded buffers, kept alive on purpose
 
 
-def ensure_workspace(device, nbytes: int):
-    """Register a workspace of at least ``nbytes`` on ``device`` (torch memory)."""
+class WorkspaceCaptureError(RuntimeError):
+    """A split-KV call under graph capture needs more workspace than its
+    stream holds (allocating then would give the graph memory that a later,
+    larger call could replace)."""
+
+
+def _stream_workspace(idx: int, stream_handle: int, nbytes: int):
+    """The buffer of (device, stream), grown to at least ``nbytes``
+    outside graph capture.  Call with _ws_lock held."""
+    import torch
+
+    key = (idx, int(stream_handle or 0))
+    buf = _workspaces.get(key)
+    if buf is not None and buf.numel() >= nbytes:
+        return buf
+    if torch.cuda.is_current_stream_capturing():
+        have = 0 if buf is None else buf.numel()
+        raise WorkspaceCaptureError(
+            f"split-KV workspace of {nbytes} bytes needed while capturing a graph, but this stream holds "
+            f"{have}: run the same shape once on the capture stream before capturing, or call "
+            "reserve_workspace(device, nbytes, stream) first")
+    new = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=torch.device("cuda", idx))
+    if buf is not None:
+        _retired.append(buf)
+    _workspaces[key] = new
+    return new
+
+
+def _register(idx: int, buf) -> None:
+    import torch
+
+    with torch.cuda.device(idx):
+        rc = fa_set_workspace(buf.data_ptr(), buf.numel())
+    if rc != FA_OK:
+        raise FAError(rc, "fa_set_workspace")
+
+
+def reserve_workspace(device, nbytes: int, stream=None):
+    """Reserve (never release) a split-KV workspace of at least ``nbytes``
+    for ``stream`` (a torch.cuda.Stream or raw handle; default: the current
+    stream of ``device``) and register it with the library, for callers of
+    the raw C entry points.  Returns the buffer, or None when ``nbytes`` is 0."""
     import torch
 
     if nbytes <= 0:
         return None
     idx = device.index if device.index is not None else torch.cuda.current_device()
-    buf = _workspaces.get(idx)
-    if buf is None or buf.numel() < nbytes:
-        buf = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=torch.device("cuda", idx))
-        with torch.cuda.device(idx):
-            rc = fa_set_workspace(buf.data_ptr(), buf.numel())
-        if rc != FA_OK:
-            raise FAError(rc, "fa_set_workspace")
-        _workspaces[idx] = buf
+    if stream is None:
+        handle = torch.cuda.current_stream(idx).cuda_stream
+    else:
+        handle = getattr(stream, "cuda_stream", stream)
+    with _ws_lock:
+        buf = _stream_workspace(idx, handle, nbytes)
+        _register(idx, buf)
     return buf
+
+
+def _call_with_workspace(dev, stream_handle, nbytes, fn):
+    """fn() with the workspace of (device, stream) registered, atomically
+    with respect to other calls of this module."""
+    import torch
+
+    if nbytes <= 0:
+        return fn()
+    idx = dev.index if dev.index is not None else torch.cuda.current_device()
+    with _ws_lock:
+        _register(idx, _stream_workspace(idx, stream_handle, nbytes))
+        return fn()
 
 
 def attention(q, k, v, *, causal=False, seqused_k=None, scale=None, out=None, lse=None,
@@ -242,17 +305,21 @@ def attention(q, k, v, *, causal=False, seqused_k=None, scale=None, out=None, ls
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
         if variant is not None:
-            ensure_workspace(dev, fa_fwd_variant_workspace_bytes(B, Sq, Sk, Hq, Hkv, D, causal, *variant))
-            rc = fa_fwd_variant(*ptrs, B, Sq, Sk, Hq, Hkv, D, causal, sq, float(scale), *variant, stream)
+            rc = _call_with_workspace(
+                dev, stream, fa_fwd_variant_workspace_bytes(B, Sq, Sk, Hq, Hkv, D, causal, *variant),
+                lambda: fa_fwd_variant(*ptrs, B, Sq, Sk, Hq, Hkv, D, causal, sq, float(scale), *variant, stream))
             where = "fa_fwd_variant"
         elif dense:
-            ensure_workspace(dev, fa_fwd_workspace_bytes(B, Sq, Sk, Hq, Hkv, D, causal))
-            rc = fa_fwd(*ptrs, B, Sq, Sk, Hq, Hkv, D, causal, sq, float(scale), stream)
+            rc = _call_with_workspace(
+                dev, stream, fa_fwd_workspace_bytes(B, Sq, Sk, Hq, Hkv, D, causal),
+                lambda: fa_fwd(*ptrs, B, Sq, Sk, Hq, Hkv, D, causal, sq, float(scale), stream))
             where = "fa_fwd"
         else:
-            ensure_workspace(dev, fa_fwd_workspace_bytes(B, Sq, Sk, Hq, Hkv, D, causal))
-            rc = fa_fwd_strided(*ptrs, B, Sq, Sk, Hq, Hkv, D, q.stride()[:3], k.stride()[:3], v.stride()[:3],
-                                out.stride()[:3], dtypes[q.dtype], causal, sq, float(scale), stream)
+            rc = _call_with_workspace(
+                dev, stream, fa_fwd_workspace_bytes(B, Sq, Sk, Hq, Hkv, D, causal),
+                lambda: fa_fwd_strided(*ptrs, B, Sq, Sk, Hq, Hkv, D, q.stride()[:3], k.stride()[:3],
+                                       v.stride()[:3], out.stride()[:3], dtypes[q.dtype], causal, sq,
+                                       float(scale), stream))
             where = "fa_fwd_strided"
     if rc != FA_OK:
         raise FAError(rc, where)
@@ -302,10 +369,11 @@ def attention_nvfp4(q, k, v, *, causal=False, seqused_k=None, scale=None, out_fp
     sq = 0 if seqused_k is None else seqused_k.data_ptr()
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
-        ensure_workspace(dev, fa_fwd_workspace_bytes(B, Sq, Sk, Hq, Hkv, D, causal))
-        rc = fa_fwd_nvfp4(q.data_ptr(), k.data_ptr(), v.data_ptr(), bufs["out_fp4"].data_ptr(),
-                          bufs["out_sf"].data_ptr(), 0 if lse is None else lse.data_ptr(), B, Sq, Sk, Hq, Hkv, D,
-                          causal, sq, float(scale), stream)
+        rc = _call_with_workspace(
+            dev, stream, fa_fwd_workspace_bytes(B, Sq, Sk, Hq, Hkv, D, causal),
+            lambda: fa_fwd_nvfp4(q.data_ptr(), k.data_ptr(), v.data_ptr(), bufs["out_fp4"].data_ptr(),
+                                 bufs["out_sf"].data_ptr(), 0 if lse is None else lse.data_ptr(), B, Sq, Sk, Hq,
+                                 Hkv, D, causal, sq, float(scale), stream))
     if rc != FA_OK:
         raise FAError(rc, "fa_fwd_nvfp4")
     return bufs["out_fp4"], bufs["out_sf"], lse
@@ -358,11 +426,12 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seql
     causal = bool(causal)
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
-        ensure_workspace(dev, fa_fwd_workspace_bytes(B, int(max_seqlen_q), int(max_seqlen_k), Hq, Hkv, D, causal))
-        rc = fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                           0 if lse is None else lse.data_ptr(), cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(),
-                           B, int(max_seqlen_q), int(max_seqlen_k), total_q, total_k, Hq, Hkv, D, dtypes[q.dtype],
-                           causal, float(scale), stream)
+        rc = _call_with_workspace(
+            dev, stream, fa_fwd_workspace_bytes(B, int(max_seqlen_q), int(max_seqlen_k), Hq, Hkv, D, causal),
+            lambda: fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                  0 if lse is None else lse.data_ptr(), cu_seqlens_q.data_ptr(),
+                                  cu_seqlens_k.data_ptr(), B, int(max_seqlen_q), int(max_seqlen_k), total_q, total_k,
+                                  Hq, Hkv, D, dtypes[q.dtype], causal, float(scale), stream))
     if rc != FA_OK:
         raise FAError(rc, "fa_fwd_varlen")
     return out, lse

@@ -52,7 +52,9 @@ enum {
   FA_ERR_SCALE = 5,       /* scale not finite or not > 0 */
   FA_ERR_WORKSPACE = 6,   /* the split-KV path needs a workspace that is missing or too small */
   FA_ERR_LAUNCH = 7,      /* the HIP runtime rejected a kernel launch */
-  FA_ERR_ALIAS = 8        /* out overlaps q, k or v, or lse overlaps one of them */
+  FA_ERR_ALIAS = 8        /* out or lse overlaps q, k, v, seqused_k or cu_seqlens_q/k, or lse
+                             overlaps out (outputs are written while other workgroups still
+                             read the inputs) */
 };
 
 /* fa_fwd: one attention forward pass.
@@ -127,7 +129,7 @@ enum {
  * (k_ss, v_ss >= D when Sk > 1) and no two output rows overlap
  * (FA_ERR_SHAPE); Sk*k_ss*2 and Sk*v_ss*2 bytes, and the bytes from a
  * batch entry's first query row to its last, below 2^31 (FA_ERR_SHAPE);
- * out and lse must not share a byte with the span of q, k or v
+ * out and lse must not share a byte with the span of q, k, v or seqused_k
  * (FA_ERR_ALIAS).  q, k and v may share memory (e.g. one fused QKV buffer).
  */
 int fa_fwd_strided(const void* q, const void* k, const void* v, void* out, float* lse,
@@ -166,7 +168,8 @@ int fa_fwd_strided(const void* q, const void* k, const void* v, void* out, float
  * Workspace: fa_fwd_workspace_bytes(B, max_seqlen_q, max_seqlen_k, Hq, Hkv,
  * D, causal).  Checks and codes as for fa_fwd (sizes: total_q*Hq*D and
  * total_k*Hkv*D elements and max_seqlen_k*Hkv*D*2 bytes below 2^31;
- * cu_seqlens 4-byte aligned; out/lse must not overlap q, k, v). */
+ * cu_seqlens 4-byte aligned; out/lse must not overlap q, k, v or the
+ * cu_seqlens arrays). */
 int fa_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
                   const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                   int B, int max_seqlen_q, int max_seqlen_k, int total_q, int total_k,
@@ -207,8 +210,8 @@ int fa_set_workspace(void* dev_ptr, size_t bytes);
  * contiguous; D must be 64 or 256 (a multiple of 16 with a compiled
  * variant; FA_ERR_UNSUPPORTED otherwise).  Everything else (lse,
  * seqused_k, causal, scale, stream, workspace, checks and codes) is as for
- * fa_fwd; out_fp4, out_sf and lse must not overlap each other or q, k, v
- * (FA_ERR_ALIAS). */
+ * fa_fwd; out_fp4, out_sf and lse must not overlap each other or q, k, v,
+ * seqused_k (FA_ERR_ALIAS). */
 int fa_fwd_nvfp4(const void* q, const void* k, const void* v, void* out_fp4, void* out_sf, float* lse,
                  int B, int Sq, int Sk, int Hq, int Hkv, int D, int causal,
                  const int32_t* seqused_k, float scale, hipStream_t stream);

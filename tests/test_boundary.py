@@ -82,6 +82,9 @@ def _call(**over):
     (dict(out=K + 4096), fa.FA_ERR_ALIAS),
     (dict(lse=V), fa.FA_ERR_ALIAS),
     (dict(lse=O + 1024), fa.FA_ERR_ALIAS),
+    (dict(seqused_k=O + 4096), fa.FA_ERR_ALIAS),      # inside out
+    (dict(seqused_k=L + 16), fa.FA_ERR_ALIAS),        # inside lse
+    (dict(seqused_k=L - 4, B=2), fa.FA_ERR_ALIAS),    # its second entry is lse's first
 ])
 def test_invalid_arguments_return_their_code(lib, over, code):
     assert _call(**over) == code
@@ -110,6 +113,8 @@ def _call_strided(qs=None, ks=None, vs=None, os_=None, dtype=fa.FA_BF16, **over)
     (dict(q=Q + 8), fa.FA_ERR_ALIGN),
     (dict(out=Q), fa.FA_ERR_ALIAS),
     (dict(lse=K + 64), fa.FA_ERR_ALIAS),
+    (dict(seqused_k=O + 64), fa.FA_ERR_ALIAS),
+    (dict(seqused_k=L), fa.FA_ERR_ALIAS),
     # element type
     (dict(dtype=2), fa.FA_ERR_UNSUPPORTED),
     (dict(dtype=-1), fa.FA_ERR_UNSUPPORTED),
@@ -167,6 +172,8 @@ def _call_varlen(**over):
     (dict(lse=L + 1), fa.FA_ERR_ALIGN),
     (dict(out=Q + 1024), fa.FA_ERR_ALIAS),
     (dict(lse=O + 4096), fa.FA_ERR_ALIAS),
+    (dict(cu_q=O + 64), fa.FA_ERR_ALIAS),
+    (dict(cu_k=L + 8), fa.FA_ERR_ALIAS),
 ])
 def test_varlen_invalid_arguments_return_their_code(lib, over, code):
     assert _call_varlen(**over) == code
@@ -287,6 +294,9 @@ def _call_nvfp4(**over):
     (dict(sf=K + 64), fa.FA_ERR_ALIAS),
     (dict(sf=O + 1024), fa.FA_ERR_ALIAS),            # inside the codes (64 rows x 128 bytes)
     (dict(lse=O + 4096), fa.FA_ERR_ALIAS),
+    (dict(seqused_k=O + 64), fa.FA_ERR_ALIAS),       # inside the codes
+    (dict(seqused_k=O + (1 << 24) + 8), fa.FA_ERR_ALIAS),   # inside the scales
+    (dict(seqused_k=L + 4), fa.FA_ERR_ALIAS),
 ])
 def test_nvfp4_invalid_arguments_return_their_code(lib, over, code):
     assert _call_nvfp4(**over) == code
