@@ -17,6 +17,7 @@ from .fa import (  # noqa: F401
     fa_fwd,
     fa_fwd_nvfp4,
     fa_fwd_plan,
+    fa_fwd_static,
     fa_fwd_strided,
     fa_fwd_variant,
     fa_fwd_variant_workspace_bytes,
@@ -40,6 +41,7 @@ __all__ = [
     "fa_fwd",
     "fa_fwd_nvfp4",
     "fa_fwd_plan",
+    "fa_fwd_static",
     "fa_fwd_strided",
     "fa_fwd_variant",
     "fa_fwd_variant_workspace_bytes",

@@ -20,6 +20,8 @@
 #include "../../include/fa.h"
 #include "fa_launch.h"
 
+static_assert(fa::kStaticScratchBytes == FA_STATIC_SCRATCH_BYTES, "one size for the static split scratch");
+
 namespace {
 
 constexpr int kMaxDevices = 64;
@@ -361,10 +363,14 @@ struct Packed {
   int total_q = 0, total_k = 0;
 };
 
+// Where the split-KV partials of a call go: the workspace registered for
+// the current device, or the library's static scratch (fa_fwd_static).
+enum class Scratch { kRegistered, kStatic };
+
 int run(const Plan& pl, const void* q, const void* k, const void* v, void* out, float* lse, int B, int Sq,
         int Sk, int Hq, int Hkv, const View& vq, const View& vk, const View& vv, const View& vo,
         const int32_t* seqused_k, float scale, hipStream_t stream, const Packed& packed = Packed(),
-        void* fp4_out = nullptr, void* fp4_sf = nullptr) {
+        void* fp4_out = nullptr, void* fp4_sf = nullptr, Scratch where = Scratch::kRegistered) {
   fa::FwdParams p{};
   p.fp4_out = static_cast<uint8_t*>(fp4_out);
   p.fp4_sf = static_cast<uint8_t*>(fp4_sf);
@@ -406,10 +412,14 @@ int run(const Plan& pl, const void* q, const void* k, const void* v, void* out, 
   p.v_sb = vv.sb, p.v_ss = vv.ss, p.v_sh = vv.sh;
   p.o_sb = vo.sb, p.o_ss = vo.ss, p.o_sh = vo.sh;
   if (pl.launch.split) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FA_ERR_LAUNCH;
     Workspace ws;
-    {
+    if (where == Scratch::kStatic) {
+      if (pl.ws_bytes > fa::kStaticScratchBytes) return FA_ERR_SCRATCH;
+      if (fa::static_scratch(&ws.ptr) != hipSuccess) return FA_ERR_LAUNCH;
+      ws.bytes = fa::kStaticScratchBytes;
+    } else {
+      int dev = 0;
+      if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FA_ERR_LAUNCH;
       std::lock_guard<std::mutex> lock(g_ws_mu);
       ws = g_ws[dev];
     }
@@ -441,6 +451,7 @@ const char* fa_status_string(int code) {
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: split-KV path needs a registered workspace of fa_fwd_workspace_bytes() bytes";
     case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: the HIP runtime reported an error";
     case FA_ERR_ALIAS: return "FA_ERR_ALIAS: out or lse overlaps an input (q, k, v, seqused_k, cu_seqlens) or each other";
+    case FA_ERR_SCRATCH: return "FA_ERR_SCRATCH: fa_fwd_static: this shape's split-KV partials exceed the 8 MiB static scratch (use fa_fwd with a registered workspace)";
     default: return "FA_ERR_UNKNOWN: unknown status code";
   }
 }
@@ -475,6 +486,16 @@ int fa_fwd(const void* q, const void* k, const void* v, void* out, float* lse, i
   const Plan pl = default_plan(B, Sq, Sk, Hq, Hkv, D, causal);
   return run(pl, q, k, v, out, lse, B, Sq, Sk, Hq, Hkv, contiguous(Sq, Hq, D), contiguous(Sk, Hkv, D),
              contiguous(Sk, Hkv, D), contiguous(Sq, Hq, D), seqused_k, scale, stream);
+}
+
+int fa_fwd_static(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Sq, int Sk,
+                  int Hq, int Hkv, int D, int causal, const int32_t* seqused_k, float scale, hipStream_t stream) {
+  int rc = check_args(q, k, v, out, lse, B, Sq, Sk, Hq, Hkv, D, causal, seqused_k, scale);
+  if (rc != FA_OK) return rc;
+  const Plan pl = default_plan(B, Sq, Sk, Hq, Hkv, D, causal);
+  return run(pl, q, k, v, out, lse, B, Sq, Sk, Hq, Hkv, contiguous(Sq, Hq, D), contiguous(Sk, Hkv, D),
+             contiguous(Sk, Hkv, D), contiguous(Sq, Hq, D), seqused_k, scale, stream, Packed(), nullptr, nullptr,
+             Scratch::kStatic);
 }
 
 int fa_fwd_strided(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Sq, int Sk,

@@ -48,10 +48,41 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "fa_launch.h"
 
 namespace fa {
+
+// ----------------------------------------------------- static split scratch
+// The split-KV partials of fa_fwd_static live here instead of in a
+// caller-registered workspace, for callers that cannot allocate.  Each GPU
+// the library runs on holds its own copy for the life of the process.  In
+// host code the name `scratch` is only a host-side stand-in: the device
+// address of the current GPU's copy comes from hipGetSymbolAddress, taken
+// once per device and kept.  Nothing in it has to start at zero: every
+// partial the merge kernel reads is written earlier by the same call.
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+hipError_t static_scratch(void** ptr) {
+  constexpr int kMaxDev = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDev] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));

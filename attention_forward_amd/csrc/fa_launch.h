@@ -65,6 +65,11 @@ struct LaunchPlan {
   int outf;                // OutFormat of the result
 };
 
+// Device-resident split-KV scratch of fa_fwd_static (one array per GPU,
+// in fa_kernels.hip): its size, and its address on the current device.
+constexpr size_t kStaticScratchBytes = 8u << 20;
+hipError_t static_scratch(void** ptr);
+
 bool variant_exists(int D, int qt, int nw, int kw, int bn, int nst, int dtype);
 bool nvfp4_variant_exists(const LaunchPlan& plan);
 hipError_t launch_fwd(const FwdParams& p, const LaunchPlan& plan, hipStream_t stream);

@@ -30,11 +30,13 @@ FA_ERR_SCALE = 5
 FA_ERR_WORKSPACE = 6
 FA_ERR_LAUNCH = 7
 FA_ERR_ALIAS = 8
+FA_ERR_SCRATCH = 9
+FA_STATIC_SCRATCH_BYTES = 8 << 20
 
 FA_BF16 = 0
 FA_FP16 = 1
 
-EXPORTS = ("fa_fwd", "fa_fwd_strided", "fa_fwd_varlen", "fa_fwd_nvfp4", "fa_fwd_workspace_bytes", "fa_set_workspace",
+EXPORTS = ("fa_fwd", "fa_fwd_static", "fa_fwd_strided", "fa_fwd_varlen", "fa_fwd_nvfp4", "fa_fwd_workspace_bytes", "fa_set_workspace",
            "fa_fwd_variant",
            "fa_fwd_variant_workspace_bytes", "fa_fwd_plan", "fa_status_string", "fa_abi_version")
 
@@ -64,6 +66,8 @@ def load_library():
         vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
         lib.fa_fwd.restype = i32
         lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, f32, vp]
+        lib.fa_fwd_static.restype = i32
+        lib.fa_fwd_static.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, f32, vp]
         i64 = ctypes.c_int64
         lib.fa_fwd_strided.restype = i32
         lib.fa_fwd_strided.argtypes = [vp, vp, vp, vp, vp] + [i32] * 6 + [i64] * 12 + [i32, i32, vp, f32, vp]
@@ -97,6 +101,14 @@ def fa_fwd(q, k, v, out, lse, B, Sq, Sk, Hq, Hkv, D, causal, seqused_k, scale, s
     return load_library().fa_fwd(q or None, k or None, v or None, out or None, lse or None,
                                  B, Sq, Sk, Hq, Hkv, D, int(causal), seqused_k or None,
                                  ctypes.c_float(scale), stream or None)
+
+
+def fa_fwd_static(q, k, v, out, lse, B, Sq, Sk, Hq, Hkv, D, causal, seqused_k, scale, stream) -> int:
+    """C ``fa_fwd_static`` (split-KV partials in the library's device scratch;
+    no workspace registration); pointers and stream are integers (0 for NULL)."""
+    return load_library().fa_fwd_static(q or None, k or None, v or None, out or None, lse or None,
+                                        B, Sq, Sk, Hq, Hkv, D, int(causal), seqused_k or None,
+                                        ctypes.c_float(scale), stream or None)
 
 
 def fa_fwd_strided(q, k, v, out, lse, B, Sq, Sk, Hq, Hkv, D, q_strides, k_strides, v_strides, o_strides,

@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 4
+#define FA_ABI_VERSION 5
 
 /* Status codes. */
 enum {
@@ -52,9 +52,11 @@ enum {
   FA_ERR_SCALE = 5,       /* scale not finite or not > 0 */
   FA_ERR_WORKSPACE = 6,   /* the split-KV path needs a workspace that is missing or too small */
   FA_ERR_LAUNCH = 7,      /* the HIP runtime rejected a kernel launch */
-  FA_ERR_ALIAS = 8        /* out or lse overlaps q, k, v, seqused_k or cu_seqlens_q/k, or lse
+  FA_ERR_ALIAS = 8,       /* out or lse overlaps q, k, v, seqused_k or cu_seqlens_q/k, or lse
                              overlaps out (outputs are written while other workgroups still
                              read the inputs) */
+  FA_ERR_SCRATCH = 9      /* fa_fwd_static: the shape's split-KV partials exceed the static
+                             scratch (FA_STATIC_SCRATCH_BYTES) */
 };
 
 /* fa_fwd: one attention forward pass.
@@ -95,6 +97,30 @@ enum {
 int fa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
            int B, int Sq, int Sk, int Hq, int Hkv, int D, int causal,
            const int32_t* seqused_k, float scale, hipStream_t stream);
+
+/* fa_fwd_static: fa_fwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Arguments, checks, plan, kernels and results are those of
+ * fa_fwd (bit for bit); the only difference is where the split-KV path keeps
+ * its partial results: in a device array inside this library, one per GPU,
+ * of FA_STATIC_SCRATCH_BYTES, instead of a workspace registered with
+ * fa_set_workspace.  It calls no allocator: the array exists from the
+ * library's load on each GPU until the process ends, and its address is
+ * looked up once per device on the first call there.
+ *   - A shape whose partials need more than FA_STATIC_SCRATCH_BYTES
+ *     (fa_fwd_workspace_bytes() tells) returns FA_ERR_SCRATCH, with nothing
+ *     queued; use fa_fwd with a registered workspace for it.  Shapes that
+ *     take the single-pass path use no scratch at all.
+ *   - Every call on one GPU shares that GPU's array: calls whose execution
+ *     overlaps in time on one GPU (different streams, or graph replays run
+ *     concurrently) race and may return wrong results.  Serialise them (one
+ *     stream).  Nothing in the array needs clearing between calls.
+ * Returns FA_OK after queueing the work, or an FA_ERR_* code (FA_ERR_LAUNCH
+ * also when the array's address cannot be obtained). */
+#define FA_STATIC_SCRATCH_BYTES (8u << 20)
+int fa_fwd_static(const void* q, const void* k, const void* v, void* out, float* lse,
+                  int B, int Sq, int Sk, int Hq, int Hkv, int D, int causal,
+                  const int32_t* seqused_k, float scale, hipStream_t stream);
 
 /* Element types of q, k, v and out (fa_fwd_strided). */
 enum {

@@ -41,8 +41,8 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert fa.fa_abi_version() == 4
-    for code in range(9):
+    assert fa.fa_abi_version() == 5
+    for code in range(10):
         assert fa.fa_status_string(code).startswith("FA_")
     assert "UNKNOWN" in fa.fa_status_string(99)
 
@@ -300,6 +300,32 @@ def _call_nvfp4(**over):
 ])
 def test_nvfp4_invalid_arguments_return_their_code(lib, over, code):
     assert _call_nvfp4(**over) == code
+
+
+def test_static_entry_point_host_checks(lib):
+    """fa_fwd_static: the argument checks of fa_fwd, and a shape whose
+    split-KV partials exceed the static scratch is refused before any
+    device work (both hold without a GPU)."""
+    def call(**over):
+        a = dict(q=Q, k=K, v=V, out=O, lse=L, B=1, Sq=64, Sk=64, Hq=8, Hkv=1, D=256, causal=0,
+                 seqused_k=0, scale=0.0625, stream=0)
+        a.update(over)
+        return fa.fa_fwd_static(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["Sq"], a["Sk"], a["Hq"],
+                                a["Hkv"], a["D"], a["causal"], a["seqused_k"], a["scale"], a["stream"])
+    assert call(q=0) == fa.FA_ERR_NULL
+    assert call(D=128) == fa.FA_ERR_UNSUPPORTED
+    assert call(scale=-1.0) == fa.FA_ERR_SCALE
+    assert call(out=Q) == fa.FA_ERR_ALIAS
+    # 8 views of 16 heads at D72, 64 rows over 2048 keys: split partials of 9.25 MiB
+    big = dict(B=8, Sq=64, Sk=2048, Hq=16, Hkv=16, D=72)
+    need = fa.fa_fwd_workspace_bytes(8, 64, 2048, 16, 16, 72, 0)
+    assert need > fa.FA_STATIC_SCRATCH_BYTES
+    assert call(**big) == fa.FA_ERR_SCRATCH
+    assert "static scratch" in fa.fa_status_string(fa.FA_ERR_SCRATCH)
+    # every workload fits (the split ones need well under the maximum)
+    from attention_forward_amd.workloads import WORKLOADS
+    for w in WORKLOADS.values():
+        assert fa.fa_fwd_workspace_bytes(w.B, w.Sq, w.Sk, w.Hq, w.Hkv, w.D, w.causal) <= fa.FA_STATIC_SCRATCH_BYTES
 
 
 def test_set_workspace_null_with_size(lib):
