@@ -476,7 +476,10 @@ __device__ __forceinline__ void pv_tile(f32x4_t (&oacc)[G::DT][QT], const uint32
 // order, and each XCD has its own L2.  For a non-causal single-pass grid
 // whose (batch, kv head) count is a multiple of 8, block n is given to
 // (batch*kv head, row block) such that every row block of one (batch, kv
-// head) lands on the same XCD and its K/V is fetched into one L2 only.
+// head) lands on the same XCD and its K/V is fetched into one L2 only, and
+// each XCD takes a contiguous run of (batch, kv head) pairs: neighbouring
+// heads share cache lines when a head row is not a multiple of 128 bytes
+// (144 bytes at D72), so a line is then fetched by one XCD, not two.
 // The grid sizes come from the launch parameters (nrb row blocks by B*Hkv),
 // not from the dispatch packet, which would take two more dependent scalar
 // loads before the first tile copy.
@@ -495,9 +498,9 @@ __device__ __forceinline__ void xcd_block(const FwdParams& p, int& bh, int& rb) 
   rb = blockIdx.x;
   const int nbh = p.B * p.Hkv;
   if ((nbh & 7) == 0) {
-    const int n = blockIdx.x + p.nrb * blockIdx.y;  // dispatch order
+    const int n = blockIdx.x + p.nrb * blockIdx.y;  // dispatch order: XCD n % 8
     const int slot = n >> 3, grp = udiv(slot, p.nrb, p.nrb_m);
-    bh = (n & 7) + 8 * grp;
+    bh = (n & 7) * (nbh >> 3) + grp;  // XCD x: pairs x*nbh/8 .. (x+1)*nbh/8 - 1
     rb = slot - grp * p.nrb;
   }
 }

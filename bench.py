@@ -297,17 +297,26 @@ def cpu_baseline(headline, workloads):
 CALIB_BYTES = 256 << 20  # device-to-device copy used to calibrate the byte counters
 
 
+STRIDED_ROWS = 1 << 17  # rows of the second calibration: one 144-byte head of a 16-head D72 row each
+
+
 def traffic_probe(w, reps, device):
-    """Eager calls of the workload plus a device-to-device copy of
-    CALIB_BYTES, for a rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE pass."""
+    """Eager calls of the workload plus two calibration kernels, for a
+    rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE pass: a device-to-device copy of
+    CALIB_BYTES (contiguous), and a negation that reads one 144-byte head row
+    out of every 2304-byte row of a [rows, 16, 72] bf16 tensor (the D72
+    head layout) into a contiguous tensor."""
     import torch
 
     r = Runner(w, device)
     src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=device).fill_(1)
     dst = torch.empty_like(src)
+    heads = torch.ones(STRIDED_ROWS, 16, 72, dtype=torch.bfloat16, device=device)
+    one_head = torch.empty(STRIDED_ROWS, 72, dtype=torch.bfloat16, device=device)
     torch.cuda.synchronize()
     for _ in range(reps):
         dst.copy_(src)
+        torch.neg(heads[:, 3, :], out=one_head)
         r.step(torch.cuda.current_stream(device).cuda_stream)
     torch.cuda.synchronize()
 
@@ -329,18 +338,25 @@ def ingest_traffic(workload, fetch_csv, write_csv, out_path=TRAFFIC_FILE):
         return vals
 
     out = {}
+    strided = {}
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         vals = per_kernel(path, counter)
-        calib = max((statistics.median(v) for k, v in vals.items() if "copyBuffer" in k or "copy" in k.lower()),
-                    default=None)
+        calib = max((statistics.median(v) for k, v in vals.items()
+                     if ("copyBuffer" in k or "copy" in k.lower()) and "neg" not in k.lower()), default=None)
         if not calib:
             raise RuntimeError(f"no calibration copy found in {path}")
         factor = CALIB_BYTES / (calib * 1024.0)
         kb = sum(statistics.median(v) for k, v in vals.items() if "fa::" in k)
         out[counter] = {"kib_per_launch": kb, "calibration_kib": calib, "factor": factor,
                         "bytes_per_launch": kb * 1024.0 * factor}
+        neg = [statistics.median(v) for k, v in vals.items() if "neg" in k.lower()]
+        if neg:
+            alg = STRIDED_ROWS * 144  # bytes read (FETCH) or written (WRITE) by the 144-byte-row negation
+            strided[counter] = {"kib": neg[0], "bytes_scaled": neg[0] * 1024.0 * factor,
+                                "algorithmic_bytes": alg, "ratio": neg[0] * 1024.0 * factor / alg}
     entry = {"kernel_sha": kernel_sha(), "fetch": out["FETCH_SIZE"], "write": out["WRITE_SIZE"],
-             "bytes_per_launch": out["FETCH_SIZE"]["bytes_per_launch"] + out["WRITE_SIZE"]["bytes_per_launch"]}
+             "bytes_per_launch": out["FETCH_SIZE"]["bytes_per_launch"] + out["WRITE_SIZE"]["bytes_per_launch"],
+             "strided_144B_calibration": strided or None}
     try:
         with open(out_path) as f:
             table = json.load(f)
