@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB_NAME = "libfa_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["fa_api.cpp", "fa_kernels.hip"]
+SOURCES = ["fa_api.cpp", "fa_kernels.hip"]  # the library; csrc/intake_probe.hip is a separate executable
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -43,6 +43,27 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the ROCm toolchain is needed to build the attention library")
 
 
+PROBE_SRC = os.path.join(CSRC, "intake_probe.hip")
+PROBE_PATH = os.path.join(PKG, "intake_probe")
+
+
+def build_probe(verbose: bool = False) -> str:
+    """Compile the compute-unit intake probe (a standalone executable that
+    bench.py --intake-probe runs); returns its path."""
+    tmp = PROBE_PATH + ".tmp"
+    flags = [f for f in HIPCC_FLAGS if f not in ("-fPIC", "-shared")]
+    cmd = [hipcc(), *flags, PROBE_SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "'-packed-fp32-ops' is not a recognized feature"
+    msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln]
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed on the intake probe:\n" + "\n".join(msgs))
+    os.replace(tmp, PROBE_PATH)
+    return PROBE_PATH
+
+
 def build(verbose: bool = False) -> str:
     """Compile every source into the shared library; returns its path."""
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
@@ -60,6 +81,7 @@ def build(verbose: bool = False) -> str:
     if verbose and msgs:
         print("\n".join(msgs))
     os.replace(tmp, LIB_PATH)
+    build_probe(verbose)
     return LIB_PATH
 
 

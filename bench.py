@@ -452,6 +452,21 @@ def extension_rows(device, steps=200):
     return rows
 
 
+def intake_probe():
+    """Run the intake probe built next to the library (attention_forward_amd/intake_probe) as a child
+    process and print its JSON line."""
+    import subprocess
+
+    exe = os.path.join(ROOT, "attention_forward_amd", "intake_probe")
+    if not os.path.exists(exe):
+        print(f"{exe} is missing: run the build step first", file=sys.stderr)
+        return 1
+    res = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    sys.stdout.write(res.stdout)
+    sys.stderr.write(res.stderr)
+    return res.returncode
+
+
 def _progress(msg):
     print(f"bench: {msg}", file=sys.stderr, flush=True)
 
@@ -475,12 +490,16 @@ def main(argv=None):
                     help="skip the replay statistics and the cold-cache timing (for profiler runs)")
     ap.add_argument("--traffic-probe", type=int, default=0, metavar="REPS",
                     help="only run REPS eager calls plus a calibration copy (for rocprofv3 --pmc)")
+    ap.add_argument("--intake-probe", action="store_true",
+                    help="only run the compute-unit intake probe (bytes per clock from L2) and print its JSON")
     ap.add_argument("--ingest-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter CSVs into profiles/traffic.json and exit")
     a = ap.parse_args(argv)
     if a.ingest_traffic:
         print(json.dumps(ingest_traffic(a.workload, *a.ingest_traffic)))
         return 0
+    if a.intake_probe:
+        return intake_probe()
     if a.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {a.gpus} is not supported (this library has no "
               "multi-GPU path; run with --gpus 1)", file=sys.stderr)
