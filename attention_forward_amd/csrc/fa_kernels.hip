@@ -104,6 +104,24 @@ constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) 
 // s_waitcnt immediate with lgkmcnt = 0 (every LDS access of this wave has
 // completed) and vmcnt / expcnt left at their maxima.
 constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
+// s_waitcnt with lgkmcnt = n (0..15; larger waits for none) and vmcnt /
+// expcnt at their maxima.  The immediate must be a constant: in an unrolled
+// loop n is one, and the switch folds to a single instruction.
+constexpr int waitcnt_lgkm(int n) { return 15 | (3 << 14) | (7 << 4) | (n << 8); }
+__device__ __forceinline__ void wait_lgkm(int n) {
+  switch (n) {
+#define FA_WAIT_LGKM(n_)                                   \
+  case n_:                                                 \
+    __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(n_));          \
+    break;
+    FA_WAIT_LGKM(0) FA_WAIT_LGKM(1) FA_WAIT_LGKM(2) FA_WAIT_LGKM(3) FA_WAIT_LGKM(4) FA_WAIT_LGKM(5)
+    FA_WAIT_LGKM(6) FA_WAIT_LGKM(7) FA_WAIT_LGKM(8) FA_WAIT_LGKM(9) FA_WAIT_LGKM(10) FA_WAIT_LGKM(11)
+    FA_WAIT_LGKM(12) FA_WAIT_LGKM(13) FA_WAIT_LGKM(14)
+#undef FA_WAIT_LGKM
+    default:
+      break;
+  }
+}
 
 __device__ __forceinline__ u32x4_t ldg16(const uint16_t* p) { return *reinterpret_cast<const u32x4_t*>(p); }
 
@@ -1073,18 +1091,44 @@ fwd_kernel(const FwdParams p) {
 // different rows and share tiles), a workgroup covers KW times fewer rows, so
 // a small number of rows still fills the chip, while each wave keeps 16*QT
 // rows against every K/V byte it reads from LDS.
-template <int D, int QT, int KW, int BN, bool CAUSAL, bool SPLIT, int DTY, int OUTF>
+//
+// NST selects the buffer scheme of each wave.  NST == 1: one K and one V
+// tile buffer in padded row-major layout; a buffer is refilled after the
+// whole tile has been read.  NST == 2 (piecewise refill): the buffers are
+// cut into 1 KiB pieces, each the target of one copy instruction, and the
+// copy of the next tile's piece is issued as soon as this tile's reads of
+// that piece have returned.  A wave then keeps about one tile of K and V in
+// flight at all times instead of part of one, which is what the compute
+// unit's intake from L2 needs at head dim 256 (its latency is about 1000
+// clocks, so streaming at ~56 bytes per clock takes ~56 KiB in flight per
+// compute unit).  Pieces, for 32-key tiles:
+//   K piece (c, mt): keys 16mt .. 16mt+15, head-dim 32c .. 32c+31, 64 bytes
+//     per key; the 16-byte quarter q of key k sits at quarter q ^ (k/4 % 4)
+//     of its row, so the 16 keys one fragment read takes at one quarter
+//     fall in 16 different bank groups;
+//   V piece e: keys 0 .. 31, head-dim 32e .. 32e+31, 64 bytes per key; the
+//     16-byte quarter q of key k sits at quarter q ^ 2(k/4 % 2), so the
+//     transpose reads of 8 keys at one 16-element column hit 64 different
+//     banks.
+// Copies of 64-byte row segments run at the full intake rate (32-byte
+// segments at about half).
+template <int D, int QT, int KW, int BN, int NST, bool CAUSAL, bool SPLIT, int DTY, int OUTF>
 __global__ void __launch_bounds__(KW * 64, 1)
 fwd_ks_kernel(const FwdParams p) {
   using G = Geo<D, QT, 1, BN, DTY>;  // per-wave geometry: one wave issues its own tile copies
   constexpr int ROWS = 16 * QT;
+  constexpr bool PIECES = NST == 2;
   pin_params(p);
+  static_assert(NST == 1 || NST == 2, "buffer scheme");
   static_assert(!G::TRASH, "per-wave tiles must be whole 64-slot windows");
+  static_assert(!PIECES || (BN == 32 && D % 32 == 0), "piecewise refill: 32-key tiles, whole 32-element K steps");
   // LDS: KW per-wave K/V buffers, then the workgroup's Q tile (rows at the K
   // stride, read like K fragments); after the main loop the same memory is
   // the merge area.
+  constexpr int K_PIECES = G::KC * G::MT, V_PIECES = G::DT / 2;  // 1 KiB K pieces, 2 KiB V pieces
+  constexpr int WAVE_B = PIECES ? (K_PIECES + 2 * V_PIECES) * 1024 : G::STAGE_B;
   constexpr int Q_INSTR = round_up(ROWS * (G::KSTR / 16), 64) / 64;  // 1 KiB copies of the Q tile
-  constexpr int Q_OFF = KW * G::STAGE_B;
+  constexpr int Q_OFF = KW * WAVE_B;
   constexpr int OSTR = D * 4 + 16;                       // merge area: bytes per O row (padded)
   constexpr int MERGE_B = KW * ROWS * OSTR + KW * ROWS * 8;
   constexpr int TILE_B = Q_OFF + Q_INSTR * 1024;
@@ -1158,8 +1202,8 @@ fwd_ks_kernel(const FwdParams p) {
     const int row = P / (G::VSTR / 16), ch = P - row * (G::VSTR / 16);
     voff_v[j] = (ch < G::CPR) ? row * rstride_v + ch * 16 : kOutOfRange;
   }
-  uint8_t* kbuf = smem + wave * G::STAGE_B;
-  uint8_t* vbuf = kbuf + G::K_B;
+  uint8_t* kbuf = smem + wave * WAVE_B;
+  uint8_t* vbuf = kbuf + (PIECES ? K_PIECES * 1024 : G::K_B);
   const uint32_t lds_k = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)kbuf);
   const uint32_t lds_v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)vbuf);
   // A buffer is refilled only after this wave's reads of it have returned.
@@ -1204,12 +1248,40 @@ fwd_ks_kernel(const FwdParams p) {
       copy16_to_lds(rq, off, __builtin_amdgcn_readfirstlane(lds_q + j * 1024));
     }
   }
+  // Piecewise refill: lane l of a piece copy fills quarter slot l % 4 of
+  // key l / 4 of its 16 keys (with the quarter swizzles above).  `toff` is
+  // the tile's byte offset in the buffer range, or kOutOfRange (past the
+  // range: the copy writes zeros and reads no memory).
+  const uint32_t pk_lane = (uint32_t)(lane >> 2) * rstride_k + ((uint32_t)((lane & 3) ^ ((lane >> 4) & 3)) << 4);
+  const uint32_t pv_lane = (uint32_t)(lane >> 2) * rstride_v + ((uint32_t)((lane & 3) ^ (((lane >> 4) & 1) << 1)) << 4);
+  auto copy_k_piece = [&](uint32_t toff, int c, int mt) __attribute__((always_inline)) {
+    copy16_to_lds(rk, pk_lane + (toff + (uint32_t)(16 * mt) * rstride_k + (uint32_t)(c * 64)),
+                  lds_k + (c * G::MT + mt) * 1024);
+  };
+  auto copy_v_piece = [&](uint32_t toff, int e, int h) __attribute__((always_inline)) {
+    copy16_to_lds(rv, pv_lane + (toff + (uint32_t)(16 * h) * rstride_v + (uint32_t)(e * 64)),
+                  lds_v + (2 * e + h) * 1024);
+  };
+
   // First K and V tiles after Q: waiting for all but the V copies then means
   // Q and K have landed, and the first QK^T overlaps the V copies.
   if (nown > 0) {
-    issue_k(kbeg + wave * BN);
-    issue_v(kbeg + wave * BN);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(G::LPT_V));
+    if constexpr (PIECES) {
+      const int kt0 = kbeg + wave * BN;
+#pragma unroll
+      for (int c = 0; c < G::KC; ++c)
+#pragma unroll
+        for (int mt = 0; mt < G::MT; ++mt) copy_k_piece((uint32_t)kt0 * rstride_k, c, mt);
+#pragma unroll
+      for (int e = 0; e < V_PIECES; ++e)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) copy_v_piece((uint32_t)kt0 * rstride_v, e, h);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(K_PIECES + 2 * V_PIECES));  // this wave's Q copies landed
+    } else {
+      issue_k(kbeg + wave * BN);
+      issue_v(kbeg + wave * BN);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(G::LPT_V));
+    }
   } else {
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   }
@@ -1238,6 +1310,105 @@ fwd_ks_kernel(const FwdParams p) {
   // 18.1 -> 16.0 us (4 x 64 clocks per wave index; 8 and 12 x 64 lose
   // part of the gain).
   for (int z = 0; z < wave; ++z) __builtin_amdgcn_s_sleep(4);
+  if constexpr (PIECES) {
+    // Reads of this lane: K fragment (key col of a piece, quarter grp
+    // swizzled), V transpose read (key 4grp + r of a half, head-dim 4q of a
+    // 16-element column u of the piece: quarter 2u + q/2, swizzled by the
+    // key, which is 2(grp % 2) here).
+    const uint32_t kr_lane = (uint32_t)(col * 4 + (grp ^ ((col >> 2) & 3))) * 16;
+    const uint32_t vr_row = (uint32_t)((4 * grp + ((lane >> 2) & 3)) * 64 + ((lane & 3) >> 1) * 16 + (lane & 1) * 8);
+    const uint8_t* kb = kbuf + kr_lane;
+    const uint8_t* vb0 = vbuf + vr_row + 32 * (grp & 1);        // column u = 0
+    const uint8_t* vb1 = vbuf + vr_row + 32 * (1 - (grp & 1));  // column u = 1
+    // Copies retire in order.  Before a K piece of tile i is read, the copies
+    // issued after it are at most: the rest of K(i), all of V(i), and the K
+    // pieces of tile i+1 issued so far (PF fewer than the pieces read), so
+    // waiting for WK outstanding guarantees it; likewise WV before a V read.
+    constexpr int PF = 3;   // K steps whose fragments are read ahead of their MFMAs
+    constexpr int PFV = 6;  // V fragments read ahead
+    constexpr int WK = 2 * (G::KC - 1) + 2 * V_PIECES - 2 * PF;
+    constexpr int WV = 2 * (V_PIECES - 1) + K_PIECES - PFV;
+    static_assert(PFV % 2 == 0, "V reads run ahead by whole pieces");
+    static_assert(G::MT == 2 && G::KVC == 1 && WK >= 0 && WV >= 0 && WK < 64 && WV < 64, "piece wait counts");
+    auto read_k = [&](int c, int mt) __attribute__((always_inline)) -> typename G::E::v8 {
+      return G::E::cast(*reinterpret_cast<const u32x4_t*>(kb + (c * G::MT + mt) * 1024));
+    };
+    auto read_v = [&](int dt) __attribute__((always_inline)) -> typename G::E::v8 {
+      const uint8_t* vb = ((dt & 1) ? vb1 : vb0) + (dt >> 1) * 2048;
+      const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)vb);
+      const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vb + 1024));
+      const u32x4_t vw = {__builtin_bit_cast(u32x2_t, lo)[0], __builtin_bit_cast(u32x2_t, lo)[1],
+                          __builtin_bit_cast(u32x2_t, hi)[0], __builtin_bit_cast(u32x2_t, hi)[1]};
+      return G::E::cast(vw);
+    };
+    for (int i = 0; i < nown; ++i) {
+      const int kt = kbeg + (wave + i * KW) * BN;
+      // the next tile of this wave, or (last tile) copies that read nothing,
+      // which keep the wait counts of every tile the same
+      const bool next = i + 1 < nown;
+      const uint32_t tk = next ? (uint32_t)(kt + KW * BN) * rstride_k : kOutOfRange;
+      const uint32_t tv = next ? (uint32_t)(kt + KW * BN) * rstride_v : kOutOfRange;
+      f32x4_t sacc[G::MT][QT];
+#pragma unroll
+      for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+        for (int t = 0; t < QT; ++t) sacc[mt][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      typename G::E::v8 kf[G::KC][G::MT];
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(WK));
+#pragma unroll
+      for (int c = 0; c < PF; ++c)
+#pragma unroll
+        for (int mt = 0; mt < G::MT; ++mt) kf[c][mt] = read_k(c, mt);
+#pragma unroll
+      for (int c = 0; c < G::KC; ++c) {
+        if (c + PF < G::KC) {
+          __builtin_amdgcn_s_waitcnt(waitcnt_vm(WK));
+#pragma unroll
+          for (int mt = 0; mt < G::MT; ++mt) kf[c + PF][mt] = read_k(c + PF, mt);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+          for (int t = 0; t < QT; ++t) sacc[mt][t] = G::E::mfma(kf[c][mt], qf[t][c], sacc[mt][t]);
+        __builtin_amdgcn_sched_barrier(0);
+        // the reads of step c have returned (fewer than 2 PF reads issued since)
+        wait_lgkm(2 * (G::KC - 1 - c < PF ? G::KC - 1 - c : PF));
+#pragma unroll
+        for (int mt = 0; mt < G::MT; ++mt) copy_k_piece(tk, c, mt);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      uint32_t pk[G::KVC][QT][4];
+      softmax_tile<G, QT, CAUSAL>(sacc, pk, m_run, l_run, oacc, srow, kt, kend, s_lo, c2, grp);
+      __builtin_amdgcn_sched_barrier(0);
+      typename G::E::v8 vf[G::DT];
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(WV));
+#pragma unroll
+      for (int dt = 0; dt < PFV; ++dt) vf[dt] = read_v(dt);
+#pragma unroll
+      for (int dt = 0; dt < G::DT; ++dt) {
+        if (dt + PFV < G::DT) {
+          __builtin_amdgcn_s_waitcnt(waitcnt_vm(WV));
+          vf[dt + PFV] = read_v(dt + PFV);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < QT; ++t) {
+          const u32x4_t pw = {pk[0][t][0], pk[0][t][1], pk[0][t][2], pk[0][t][3]};
+          oacc[dt][t] = G::E::mfma(vf[dt], G::E::cast(pw), oacc[dt][t]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (dt & 1) {
+          // both columns of piece dt/2 have been read
+          wait_lgkm(2 * (G::DT - 1 - dt < PFV ? G::DT - 1 - dt : PFV));
+          copy_v_piece(tv, dt >> 1, 0);
+          copy_v_piece(tv, dt >> 1, 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the last copies have landed before the LDS is reused
+  } else
   for (int i = 0; i < nown; ++i) {
     const int kt = kbeg + (wave + i * KW) * BN;
     const bool next = i + 1 < nown;
@@ -1449,7 +1620,7 @@ static hipError_t launch_variant(const FwdParams& p, const LaunchPlan& plan, hip
   return hipGetLastError();
 }
 
-template <int D, int QT, int KW, int BN, bool CAUSAL, bool SPLIT, int DTY, int OUTF = kOutElem>
+template <int D, int QT, int KW, int BN, int NST, bool CAUSAL, bool SPLIT, int DTY, int OUTF = kOutElem>
 static hipError_t launch_ks_variant(const FwdParams& p, const LaunchPlan& plan, hipStream_t stream) {
   constexpr int ROWS = 16 * QT;
   const int nrb = (p.Mp + ROWS - 1) / ROWS;
@@ -1459,7 +1630,7 @@ static hipError_t launch_ks_variant(const FwdParams& p, const LaunchPlan& plan, 
   } else {
     grid = dim3(nrb, p.B * p.Hkv, SPLIT ? plan.nsplit : 1);
   }
-  hipLaunchKernelGGL((fwd_ks_kernel<D, QT, KW, BN, CAUSAL, SPLIT, DTY, OUTF>), grid, dim3(KW * 64), 0, stream, p);
+  hipLaunchKernelGGL((fwd_ks_kernel<D, QT, KW, BN, NST, CAUSAL, SPLIT, DTY, OUTF>), grid, dim3(KW * 64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !SPLIT) return e;
   const long long threads = (long long)nrb * ROWS * (D / 4);  // per (batch, kv head)
@@ -1475,7 +1646,8 @@ static hipError_t launch_ks_variant(const FwdParams& p, const LaunchPlan& plan, 
 // has twice the waves on the same rows, each group taking every other key
 // tile, and the two partials are merged in LDS.  Key-split (fwd_ks_kernel)
 // entries: element type, head dim, rows per wave / 16, waves (all on the
-// same rows), keys per tile.  Every variant is built with and without causal
+// same rows), keys per tile, buffer scheme (1: whole-tile buffers, 2:
+// piecewise refill).  Every variant is built with and without causal
 // masking and with and without the split-KV partial output.  fp16 has the
 // variants the default plan uses.
 #define FA_VARIANTS(X)           \
@@ -1514,14 +1686,16 @@ static hipError_t launch_ks_variant(const FwdParams& p, const LaunchPlan& plan, 
   X(kF16, 256, 2, 4, 1, 32, 2)   \
   X(kF16, 256, 1, 4, 1, 64, 2)
 
-#define FA_KS_VARIANTS(X)  \
-  X(kBf16, 64, 2, 4, 64)   \
-  X(kBf16, 72, 2, 4, 64)   \
-  X(kBf16, 256, 2, 4, 32)  \
-  X(kBf16, 256, 1, 4, 32)  \
-  X(kBf16, 256, 2, 2, 32)  \
-  X(kF16, 256, 2, 4, 32)   \
-  X(kF16, 256, 1, 4, 32)
+#define FA_KS_VARIANTS(X)     \
+  X(kBf16, 64, 2, 4, 64, 1)   \
+  X(kBf16, 72, 2, 4, 64, 1)   \
+  X(kBf16, 256, 2, 4, 32, 1)  \
+  X(kBf16, 256, 1, 4, 32, 1)  \
+  X(kBf16, 256, 2, 2, 32, 1)  \
+  X(kBf16, 256, 2, 4, 32, 2)  \
+  X(kBf16, 256, 1, 4, 32, 2)  \
+  X(kF16, 256, 2, 4, 32, 2)   \
+  X(kF16, 256, 1, 4, 32, 2)
 
 // (nw, kw) of a plan: kw == 1, waves on different rows; kw == nw, every wave
 // on the same rows (key-split kernel); otherwise kw key groups of nw / kw
@@ -1536,9 +1710,8 @@ bool variant_exists(int D, int qt, int nw, int kw, int bn, int nst, int dtype) {
 #undef FA_MATCH
     return false;
   }
-  if (nst != 1) return false;
-#define FA_KS_MATCH(t_, d_, q_, k_, b_) \
-  if (dtype == t_ && D == d_ && qt == q_ && kw == k_ && bn == b_) return true;
+#define FA_KS_MATCH(t_, d_, q_, k_, b_, s_) \
+  if (dtype == t_ && D == d_ && qt == q_ && kw == k_ && bn == b_ && nst == s_) return true;
   FA_KS_VARIANTS(FA_KS_MATCH)
 #undef FA_KS_MATCH
   return false;
@@ -1555,7 +1728,7 @@ bool nvfp4_variant_exists(const LaunchPlan& l) {
                               (l.D == 256 && l.qt == 2 && l.nw == 4 && l.kw == 1 && l.bn == 32 && l.nst == 2) ||
                               (l.D == 256 && l.qt == 1 && l.nw == 4 && l.kw == 1 && l.bn == 64 && l.nst == 2) ||
                               (l.D == 256 && (l.qt == 1 || l.qt == 2) && l.nw == 4 && l.kw == 4 && l.bn == 32 &&
-                               l.nst == 1));
+                               l.nst == 2));
 }
 
 template <bool CAUSAL, bool SPLIT>
@@ -1571,8 +1744,8 @@ static hipError_t launch_nvfp4(const FwdParams& p, const LaunchPlan& plan, hipSt
   if (plan.D == 64)
     return plan.bn == 128 ? launch_variant<64, 1, 4, 128, 2, 1, CAUSAL, SPLIT, kBf16, kOutNvfp4>(p, plan, stream)
                           : launch_variant<64, 1, 4, 64, 2, 1, CAUSAL, SPLIT, kBf16, kOutNvfp4>(p, plan, stream);
-  return plan.qt == 1 ? launch_ks_variant<256, 1, 4, 32, CAUSAL, SPLIT, kBf16, kOutNvfp4>(p, plan, stream)
-                      : launch_ks_variant<256, 2, 4, 32, CAUSAL, SPLIT, kBf16, kOutNvfp4>(p, plan, stream);
+  return plan.qt == 1 ? launch_ks_variant<256, 1, 4, 32, 2, CAUSAL, SPLIT, kBf16, kOutNvfp4>(p, plan, stream)
+                      : launch_ks_variant<256, 2, 4, 32, 2, CAUSAL, SPLIT, kBf16, kOutNvfp4>(p, plan, stream);
 }
 
 hipError_t launch_fwd(const FwdParams& p, const LaunchPlan& plan, hipStream_t stream) {
@@ -1583,13 +1756,13 @@ hipError_t launch_fwd(const FwdParams& p, const LaunchPlan& plan, hipStream_t st
     return plan.split ? launch_nvfp4<false, true>(p, plan, stream) : launch_nvfp4<false, false>(p, plan, stream);
   }
   if (plan.kw > 1 && plan.kw == plan.nw) {
-#define FA_KS_DISPATCH(t_, d_, q_, k_, b_)                                                          \
-  if (plan.dtype == t_ && plan.D == d_ && plan.qt == q_ && plan.kw == k_ && plan.bn == b_) {         \
-    if (plan.causal)                                                                                \
-      return plan.split ? launch_ks_variant<d_, q_, k_, b_, true, true, t_>(p, plan, stream)        \
-                        : launch_ks_variant<d_, q_, k_, b_, true, false, t_>(p, plan, stream);      \
-    return plan.split ? launch_ks_variant<d_, q_, k_, b_, false, true, t_>(p, plan, stream)         \
-                      : launch_ks_variant<d_, q_, k_, b_, false, false, t_>(p, plan, stream);       \
+#define FA_KS_DISPATCH(t_, d_, q_, k_, b_, s_)                                                          \
+  if (plan.dtype == t_ && plan.D == d_ && plan.qt == q_ && plan.kw == k_ && plan.bn == b_ && plan.nst == s_) { \
+    if (plan.causal)                                                                                    \
+      return plan.split ? launch_ks_variant<d_, q_, k_, b_, s_, true, true, t_>(p, plan, stream)        \
+                        : launch_ks_variant<d_, q_, k_, b_, s_, true, false, t_>(p, plan, stream);      \
+    return plan.split ? launch_ks_variant<d_, q_, k_, b_, s_, false, true, t_>(p, plan, stream)         \
+                      : launch_ks_variant<d_, q_, k_, b_, s_, false, false, t_>(p, plan, stream);       \
   }
     FA_KS_VARIANTS(FA_KS_DISPATCH)
 #undef FA_KS_DISPATCH

@@ -211,28 +211,29 @@ def test_plan_and_variant_sizes(lib):
 
 def test_plan_kernel_choice(lib):
     # Head dim 256: key-split workgroups (four waves over the keys of the same
-    # 32 rows); with a row block per compute unit there is no split-KV ...
-    assert fa.fa_fwd_plan(1, 1024, 1024, 8, 1, 256, 0) == (2, 4, 4, 32, 1, 0)
-    assert fa.fa_fwd_plan(1, 2048, 2048, 8, 1, 256, 1) == (2, 4, 4, 32, 1, 0)
+    # 32 rows, piecewise refill of their tile buffers); with a row block per
+    # compute unit there is no split-KV ...
+    assert fa.fa_fwd_plan(1, 1024, 1024, 8, 1, 256, 0) == (2, 4, 4, 32, 2, 0)
+    assert fa.fa_fwd_plan(1, 2048, 2048, 8, 1, 256, 1) == (2, 4, 4, 32, 2, 0)
     # ... a padded K/V buffer runs the same plan as the unpadded keys
     assert fa.fa_fwd_plan(1, 1024, 968, 8, 1, 256, 0) == fa.fa_fwd_plan(1, 1024, 1024, 8, 1, 256, 0)
     assert fa.fa_fwd_plan(1, 41, 1009, 8, 1, 256, 0) == fa.fa_fwd_plan(1, 41, 1056, 8, 1, 256, 0)
     # ... few rows: the keys are split into fixed ranges as well, over
     # 16-row workgroups (range size from the 16-row grid: 21 blocks -> 256)
-    assert fa.fa_fwd_plan(1, 41, 1056, 8, 1, 256, 0) == (1, 4, 4, 32, 1, 256)
-    assert fa.fa_fwd_plan(1, 1, 1056, 8, 1, 256, 1) == (1, 4, 4, 32, 1, 128)    # decode: 1 block
-    assert fa.fa_fwd_plan(1, 256, 1024, 8, 1, 256, 1) == (1, 4, 4, 32, 1, 512)  # 128 blocks
-    assert fa.fa_fwd_plan(1, 512, 512, 8, 1, 256, 0) == (1, 4, 4, 32, 1, 0)   # 128 blocks: 16-row blocks, no split
-    assert fa.fa_fwd_plan(8, 41, 1056, 8, 1, 256, 0) == (1, 4, 4, 32, 1, 0)   # 168 16-row blocks: no split
+    assert fa.fa_fwd_plan(1, 41, 1056, 8, 1, 256, 0) == (1, 4, 4, 32, 2, 256)
+    assert fa.fa_fwd_plan(1, 1, 1056, 8, 1, 256, 1) == (1, 4, 4, 32, 2, 128)    # decode: 1 block
+    assert fa.fa_fwd_plan(1, 256, 1024, 8, 1, 256, 1) == (1, 4, 4, 32, 2, 512)  # 128 blocks
+    assert fa.fa_fwd_plan(1, 512, 512, 8, 1, 256, 0) == (1, 4, 4, 32, 2, 0)   # 128 blocks: 16-row blocks, no split
+    assert fa.fa_fwd_plan(8, 41, 1056, 8, 1, 256, 0) == (1, 4, 4, 32, 2, 0)   # 168 16-row blocks: no split
     assert fa.fa_fwd_plan(4, 1024, 1024, 8, 1, 256, 0) == (2, 4, 1, 32, 2, 0)  # 1024 blocks: row-split, 128 rows
     assert fa.fa_fwd_plan(2, 1024, 1024, 8, 1, 256, 0) == (1, 4, 1, 64, 2, 0)  # 512 blocks: row-split, 64 rows
-    assert fa.fa_fwd_plan(2, 2048, 2048, 8, 1, 256, 1) == (2, 4, 4, 32, 1, 0)  # causal keeps key-split
+    assert fa.fa_fwd_plan(2, 2048, 2048, 8, 1, 256, 1) == (2, 4, 4, 32, 2, 0)  # causal keeps key-split
     # ... long key buffers (over 2048 keys): about 32 power-of-two ranges per
     # row block, 32-row workgroups unless the rows fit in 16
-    assert fa.fa_fwd_plan(1, 16, 131072, 8, 1, 256, 0) == (2, 4, 4, 32, 1, 4096)
-    assert fa.fa_fwd_plan(1, 1, 32768, 8, 1, 256, 1) == (1, 4, 4, 32, 1, 1024)
+    assert fa.fa_fwd_plan(1, 16, 131072, 8, 1, 256, 0) == (2, 4, 4, 32, 2, 4096)
+    assert fa.fa_fwd_plan(1, 1, 32768, 8, 1, 256, 1) == (1, 4, 4, 32, 2, 1024)
     assert fa.fa_fwd_plan(1, 7, 65536, 2, 1, 64, 0) == (1, 4, 1, 128, 2, 2048)
-    assert fa.fa_fwd_plan(1, 256, 8192, 8, 1, 256, 1) == (2, 4, 4, 32, 1, 2048)  # 64 blocks: 4 ranges
+    assert fa.fa_fwd_plan(1, 256, 8192, 8, 1, 256, 1) == (2, 4, 4, 32, 2, 2048)  # 64 blocks: 4 ranges
     assert fa.fa_fwd_plan(1, 1, 4096, 8, 8, 64, 1) == (1, 4, 1, 128, 2, 256)     # ranges of at least 256 keys
     # Smaller head dims: row-split workgroups, 16 rows per wave
     assert fa.fa_fwd_plan(3, 256, 256, 16, 16, 72, 0) == (1, 4, 1, 128, 2, 0)   # 192 blocks: 128-key tiles
@@ -255,7 +256,8 @@ def test_variant_rejections(lib):
     args = [Q, K, V, O, L, 1, 64, 64, 8, 1, 256, 0, 0, 0.0625]
     assert fa.fa_fwd_variant(*args, 3, 4, 1, 64, 2, 0, 0) == fa.FA_ERR_UNSUPPORTED   # not compiled
     assert fa.fa_fwd_variant(*args, 1, 4, 1, 32, 3, 0, 0) == fa.FA_ERR_UNSUPPORTED   # no 3-stage build
-    assert fa.fa_fwd_variant(*args, 2, 4, 4, 32, 2, 0, 0) == fa.FA_ERR_UNSUPPORTED   # key-split: nst 1
+    assert fa.fa_fwd_variant(*args, 2, 4, 4, 32, 3, 0, 0) == fa.FA_ERR_UNSUPPORTED   # key-split: nst 1 or 2
+    assert fa.fa_fwd_variant(*args, 2, 4, 4, 64, 2, 0, 0) == fa.FA_ERR_UNSUPPORTED   # piecewise: 32-key tiles only
     assert fa.fa_fwd_variant(*args, 2, 4, 2, 32, 1, 0, 0) == fa.FA_ERR_UNSUPPORTED   # key groups: nst 2, not D256
     assert fa.fa_fwd_variant(*args, 1, 8, 2, 32, 2, 0, 0) == fa.FA_ERR_UNSUPPORTED   # key groups: not D256
     assert fa.fa_fwd_variant(*args, 1, 4, 3, 32, 2, 0, 0) == fa.FA_ERR_UNSUPPORTED   # nw not a multiple of kw

@@ -73,7 +73,7 @@ def test_causal_padding_never_read(gpu_device, case):
 
 VARIANTS = {64: [(1, 4, 1, 64, 2), (1, 4, 1, 64, 3), (2, 4, 4, 64, 1)],
             72: [(1, 4, 1, 64, 2), (1, 4, 1, 64, 3), (2, 2, 1, 64, 2), (2, 4, 4, 64, 1)],
-            256: [(1, 4, 1, 32, 2), (2, 4, 1, 32, 4), (2, 4, 4, 32, 1), (2, 2, 2, 32, 1)]}
+            256: [(1, 4, 1, 32, 2), (2, 4, 1, 32, 4), (2, 4, 4, 32, 1), (2, 4, 4, 32, 2), (1, 4, 4, 32, 2), (2, 2, 2, 32, 1)]}
 
 
 @pytest.mark.parametrize("case", [CASES[0], CASES[1], CASES[3], CASES[4], CASES[6]],
