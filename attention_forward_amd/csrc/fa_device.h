@@ -50,6 +50,26 @@ __device__ __forceinline__ void wait_lgkm(int n) {
   }
 }
 
+// s_waitcnt with vmcnt = n (0..63), for counts that are constants only after
+// unrolling (the switch then folds to one instruction).
+__device__ __forceinline__ void wait_vm(int n) {
+  switch (n) {
+#define FA_WAIT_VM(n_)                                \
+  case n_:                                            \
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(n_));       \
+    break;
+#define FA_WAIT_VM8(b_) FA_WAIT_VM(b_) FA_WAIT_VM(b_ + 1) FA_WAIT_VM(b_ + 2) FA_WAIT_VM(b_ + 3) \
+  FA_WAIT_VM(b_ + 4) FA_WAIT_VM(b_ + 5) FA_WAIT_VM(b_ + 6) FA_WAIT_VM(b_ + 7)
+    FA_WAIT_VM8(0) FA_WAIT_VM8(8) FA_WAIT_VM8(16) FA_WAIT_VM8(24)
+    FA_WAIT_VM8(32) FA_WAIT_VM8(40) FA_WAIT_VM8(48) FA_WAIT_VM8(56)
+#undef FA_WAIT_VM8
+#undef FA_WAIT_VM
+    default:
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      break;
+  }
+}
+
 __device__ __forceinline__ u32x4_t ldg16(const uint16_t* p) { return *reinterpret_cast<const u32x4_t*>(p); }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {

@@ -49,6 +49,7 @@
 
 #include <algorithm>
 #include <mutex>
+#include <type_traits>
 
 #include "fa_device.h"
 #include "fa_launch.h"
@@ -615,11 +616,8 @@ fwd_ks_kernel(const FwdParams p) {
       for (int c = 0; c < G::KC; ++c)
 #pragma unroll
         for (int mt = 0; mt < G::MT; ++mt) copy_k_piece((uint32_t)kt0 * rstride_k, c, mt);
-#pragma unroll
-      for (int e = 0; e < V_PIECES; ++e)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) copy_v_piece((uint32_t)kt0 * rstride_v, e, h);
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(K_PIECES + 2 * V_PIECES));  // this wave's Q copies landed
+      // (the first V tile streams in during the first S^T)
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(K_PIECES));  // this wave's Q copies landed
     } else {
       issue_k(kbeg + wave * BN);
       issue_v(kbeg + wave * BN);
@@ -663,16 +661,32 @@ fwd_ks_kernel(const FwdParams p) {
     const uint8_t* kb = kbuf + kr_lane;
     const uint8_t* vb0 = vbuf + vr_row + 32 * (grp & 1);        // column u = 0
     const uint8_t* vb1 = vbuf + vr_row + 32 * (1 - (grp & 1));  // column u = 1
-    // Copies retire in order.  Before a K piece of tile i is read, the copies
-    // issued after it are at most: the rest of K(i), all of V(i), and the K
-    // pieces of tile i+1 issued so far (PF fewer than the pieces read), so
-    // waiting for WK outstanding guarantees it; likewise WV before a V read.
+    // Copies retire in order, so a piece has landed once the copies issued
+    // after it are all that is outstanding.  From the second tile on, before
+    // a K piece of tile i is read those are at most: the rest of K(i), all of
+    // V(i), and the K pieces of tile i+1 issued so far (PF steps behind the
+    // reads): WK.  Likewise WV before a V read.  The first tile differs: its
+    // V pieces are issued during its own S^T (step c: V(0) piece c, then
+    // K(1) piece c), so that the S^T MFMAs overlap them; its counts follow
+    // that order (k_wait, v_wait below, exact per read).
     constexpr int PF = 3;   // K steps whose fragments are read ahead of their MFMAs
     constexpr int PFV = 6;  // V fragments read ahead
     constexpr int WK = 2 * (G::KC - 1) + 2 * V_PIECES - 2 * PF;
     constexpr int WV = 2 * (V_PIECES - 1) + K_PIECES - PFV;
     static_assert(PFV % 2 == 0, "V reads run ahead by whole pieces");
     static_assert(G::MT == 2 && G::KVC == 1 && WK >= 0 && WV >= 0 && WK < 64 && WV < 64, "piece wait counts");
+    static_assert(2 * V_PIECES == 2 * G::KC, "one V piece per K step of the first tile");
+    // first tile: K(0) piece c' (prologue) is followed by the rest of K(0) and
+    // 4 copies per S^T step issued before its read (at step c' - PF)
+    auto k_wait = [](bool first, int c_read) constexpr -> int {
+      return first ? 2 * (G::KC - 1 - c_read) + 4 * (c_read >= PF ? c_read - PF : 0) : WK;
+    };
+    // first tile: V(0) piece e is followed by K(1) piece e, the later steps'
+    // 4 copies, and the V(1) pieces issued before its read (after every
+    // second O^T step)
+    auto v_wait = [](bool first, int d_read) constexpr -> int {
+      return first ? 2 + 4 * (V_PIECES - 1 - (d_read >> 1)) + 2 * (d_read >= PFV ? (d_read - PFV) >> 1 : 0) : WV;
+    };
     auto read_k = [&](int c, int mt) __attribute__((always_inline)) -> typename G::E::v8 {
       return G::E::cast(*reinterpret_cast<const u32x4_t*>(kb + (c * G::MT + mt) * 1024));
     };
@@ -684,7 +698,8 @@ fwd_ks_kernel(const FwdParams p) {
                           __builtin_bit_cast(u32x2_t, hi)[0], __builtin_bit_cast(u32x2_t, hi)[1]};
       return G::E::cast(vw);
     };
-    for (int i = 0; i < nown; ++i) {
+    auto tile = [&](auto first_tag, int i) __attribute__((always_inline)) {
+      constexpr bool FIRST = decltype(first_tag)::value;
       const int kt = kbeg + (wave + i * KW) * BN;
       // the next tile of this wave, or (last tile) copies that read nothing,
       // which keep the wait counts of every tile the same
@@ -697,7 +712,7 @@ fwd_ks_kernel(const FwdParams p) {
 #pragma unroll
         for (int t = 0; t < QT; ++t) sacc[mt][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       typename G::E::v8 kf[G::KC][G::MT];
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(WK));
+      wait_vm(k_wait(FIRST, PF - 1));
 #pragma unroll
       for (int c = 0; c < PF; ++c)
 #pragma unroll
@@ -705,7 +720,7 @@ fwd_ks_kernel(const FwdParams p) {
 #pragma unroll
       for (int c = 0; c < G::KC; ++c) {
         if (c + PF < G::KC) {
-          __builtin_amdgcn_s_waitcnt(waitcnt_vm(WK));
+          wait_vm(k_wait(FIRST, c + PF));
 #pragma unroll
           for (int mt = 0; mt < G::MT; ++mt) kf[c + PF][mt] = read_k(c + PF, mt);
         }
@@ -715,6 +730,10 @@ fwd_ks_kernel(const FwdParams p) {
 #pragma unroll
           for (int t = 0; t < QT; ++t) sacc[mt][t] = G::E::mfma(kf[c][mt], qf[t][c], sacc[mt][t]);
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (FIRST) {
+          copy_v_piece((uint32_t)kt * rstride_v, c, 0);  // the V buffer is not read before O^T
+          copy_v_piece((uint32_t)kt * rstride_v, c, 1);
+        }
         // the reads of step c have returned (fewer than 2 PF reads issued since)
         wait_lgkm(2 * (G::KC - 1 - c < PF ? G::KC - 1 - c : PF));
 #pragma unroll
@@ -725,13 +744,13 @@ fwd_ks_kernel(const FwdParams p) {
       softmax_tile<G, QT, CAUSAL>(sacc, pk, m_run, l_run, oacc, srow, kt, kend, s_lo, c2, grp);
       __builtin_amdgcn_sched_barrier(0);
       typename G::E::v8 vf[G::DT];
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(WV));
+      wait_vm(v_wait(FIRST, PFV - 1));
 #pragma unroll
       for (int dt = 0; dt < PFV; ++dt) vf[dt] = read_v(dt);
 #pragma unroll
       for (int dt = 0; dt < G::DT; ++dt) {
         if (dt + PFV < G::DT) {
-          __builtin_amdgcn_s_waitcnt(waitcnt_vm(WV));
+          wait_vm(v_wait(FIRST, dt + PFV));
           vf[dt + PFV] = read_v(dt + PFV);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -749,7 +768,9 @@ fwd_ks_kernel(const FwdParams p) {
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-    }
+    };
+    if (nown > 0) tile(std::true_type{}, 0);
+    for (int i = 1; i < nown; ++i) tile(std::false_type{}, i);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the last copies have landed before the LDS is reused
   } else
   for (int i = 0; i < nown; ++i) {
