@@ -406,6 +406,7 @@ int run(const Plan& pl, const void* q, const void* k, const void* v, void* out, 
   p.nrb_m = 0xffffffffu / (uint32_t)pl.nrb;
   p.hkv_m = 0xffffffffu / (uint32_t)Hkv;
   p.zmax = pl.zmax;
+  p.zmax_m = 0xffffffffu / (uint32_t)std::max(pl.zmax, 1);
   p.scale_log2 = scale * 1.4426950408889634f;
   p.q_sb = vq.sb, p.q_ss = vq.ss, p.q_sh = vq.sh;
   p.k_sb = vk.sb, p.k_ss = vk.ss, p.k_sh = vk.sh;

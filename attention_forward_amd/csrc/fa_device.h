@@ -458,6 +458,15 @@ __device__ __forceinline__ int udiv(int n, int d, uint32_t m) {
   return (int)(q + ((uint32_t)n - q * (uint32_t)d >= (uint32_t)d ? 1u : 0u));
 }
 
+// Item of workgroup n in a grid of N: the dispatcher deals workgroups to
+// the 8 XCDs in turn (n goes to XCD n % 8), and this gives each XCD one
+// contiguous run of item indices (the first N % 8 XCDs one item more), so
+// neighbouring items share an L2.  A bijection of [0, N).
+__device__ __forceinline__ int xcd_run(int n, int N) {
+  const int q = N >> 3, r = N & 7, x = n & 7, j = n >> 3;
+  return x < r ? x * (q + 1) + j : r * (q + 1) + (x - r) * q + j;
+}
+
 __device__ __forceinline__ void xcd_block(const FwdParams& p, int& bh, int& rb) {
   bh = blockIdx.y;
   rb = blockIdx.x;
@@ -476,7 +485,7 @@ __device__ __forceinline__ void xcd_block(const FwdParams& p, int& bh, int& rb) 
 __device__ __forceinline__ void pin_params(const FwdParams& p) {
   asm volatile("" ::"s"(p.q_sb), "s"(p.q_ss), "s"(p.q_sh), "s"(p.k_sb), "s"(p.k_ss), "s"(p.k_sh), "s"(p.v_sb),
                "s"(p.v_ss), "s"(p.v_sh), "s"(p.o_ss), "s"(p.o_sh), "s"(p.o_sb));
-  asm volatile("" ::"s"(p.nrb), "s"(p.nrb_m), "s"(p.hkv_m), "s"(p.kps), "s"(p.coff), "s"(p.zmax), "s"(p.Mp),
+  asm volatile("" ::"s"(p.nrb), "s"(p.nrb_m), "s"(p.hkv_m), "s"(p.kps), "s"(p.coff), "s"(p.zmax), "s"(p.zmax_m), "s"(p.Mp),
                "s"(p.lse_hs), "s"(p.lse_bs), "s"(p.total_q), "s"(p.total_k));
 }
 

@@ -484,7 +484,20 @@ fwd_ks_kernel(const FwdParams p) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: wave-level addresses stay scalar
   const int col = lane & 15, grp = lane >> 4;
-  const int bh = blockIdx.y;
+  int bh = blockIdx.y;
+  int rb_nc = blockIdx.x, z_nc = SPLIT ? blockIdx.z : 0;  // non-causal row block and key range
+  if constexpr (SPLIT && !CAUSAL) {
+    // Items in (bh, key range, row block) order, each XCD taking a
+    // contiguous run of them: an XCD's L2 then holds the K/V of about
+    // N / 8 / nrb key ranges instead of all of them.
+    const int nbh = p.B * p.Hkv;
+    const int n = blockIdx.x + p.nrb * (blockIdx.y + nbh * blockIdx.z);  // dispatch order
+    const int item = xcd_run(n, p.nrb * nbh * p.zmax);
+    const int t = udiv(item, p.nrb, p.nrb_m);
+    rb_nc = item - t * p.nrb;
+    bh = udiv(t, p.zmax, p.zmax_m);
+    z_nc = t - bh * p.zmax;
+  }
   const int b = udiv(bh, p.Hkv, p.hkv_m), hk = bh - b * p.Hkv;
   const int g = p.g;
 
@@ -503,8 +516,8 @@ fwd_ks_kernel(const FwdParams p) {
     // the valid keys, up to the diagonal of the block's last row
     blk.kend = min(min(blk.kend, nvalid), (min((rb + 1) * ROWS, Mp) - 1) / g + (nvalid - sq.sq) + 1);
   } else {
-    blk.rb = blockIdx.x;
-    blk.z = SPLIT ? blockIdx.z : 0;
+    blk.rb = rb_nc;
+    blk.z = z_nc;
     blk.kbeg = SPLIT ? blk.z * p.kps : 0;
     blk.kend = SPLIT ? min(blk.kbeg + p.kps, nvalid) : nvalid;
   }

@@ -39,6 +39,7 @@ struct FwdParams {
   int nrb;                 // row blocks per (batch, kv head)
   uint32_t nrb_m, hkv_m;   // floor((2^32 - 1) / nrb) and floor((2^32 - 1) / Hkv), multipliers for udiv
   int zmax;                // most splits of any row block
+  uint32_t zmax_m;         // floor((2^32 - 1) / zmax) (split variants), multiplier for udiv
   float scale_log2;        // scale * log2(e)
   // Element strides of the views (batch, sequence, head); head_dim is
   // contiguous.  Contiguous BSHD: (S*H*D, H*D, D).
