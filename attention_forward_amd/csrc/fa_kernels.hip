@@ -473,10 +473,18 @@ fwd_ks_kernel(const FwdParams p) {
   constexpr int WAVE_B = PIECES ? (K_PIECES + 2 * V_PIECES) * 1024 : G::STAGE_B;
   constexpr int Q_INSTR = round_up(ROWS * (G::KSTR / 16), 64) / 64;  // 1 KiB copies of the Q tile
   constexpr int Q_OFF = KW * WAVE_B;
-  constexpr int OSTR = D * 4 + 16;                       // merge area: bytes per O row (padded)
-  constexpr int MERGE_B = KW * ROWS * OSTR + KW * ROWS * 8;
-  constexpr int TILE_B = Q_OFF + Q_INSTR * 1024;
-  constexpr int LDS_B = TILE_B > MERGE_B ? TILE_B : MERGE_B;
+  // Merge area: wave w's O rows go into its own K/V buffer, so a wave
+  // stores them as soon as its own tiles are done.  Rows of a power-of-two
+  // number of 256-byte bank rows are unpadded, their 16-byte chunks
+  // XOR-swizzled by the row (chunk c of row r at c ^ (r % 16)); others are
+  // padded by 16 bytes.  Either way the 16 rows one store instruction
+  // covers, and the rows and chunks one merge read covers, fall in
+  // different banks.
+  constexpr bool OSWZ = (D * 4) % 256 == 0;
+  constexpr int OSTR = OSWZ ? D * 4 : D * 4 + 16;
+  static_assert(ROWS * OSTR <= WAVE_B, "a wave's O rows fit its K/V buffer");
+  constexpr int MLS_OFF = Q_OFF + Q_INSTR * 1024;  // (m, l) per row and wave
+  constexpr int LDS_B = MLS_OFF + KW * ROWS * 8;
   static_assert(LDS_B <= 160 * 1024, "LDS of one workgroup");
   __shared__ __attribute__((aligned(16))) uint8_t smem[LDS_B];
 
@@ -808,39 +816,60 @@ fwd_ks_kernel(const FwdParams p) {
   // divided by l) and (m, l) per row; then TPR threads per row read every
   // wave's (m, l), form the weights 2^(m_w - M) / L (0 for a wave with no
   // keys) and sum the KW partials of their 16-byte chunks in wave order.
+  // A wave's own buffer is idle once its last copies have landed (waited
+  // for above) and its reads have returned (LDS operations of one wave run
+  // in order), so it stores its O there without waiting for the others.
+  auto o_chunk = [](int row, int c) constexpr -> int { return row * OSTR + (OSWZ ? (c ^ (row & 15)) : c) * 16; };
   float l_tot[QT];
 #pragma unroll
   for (int t = 0; t < QT; ++t) l_tot[t] = group_sum(l_run[t]);
-  __syncthreads();  // every wave is done with its tiles: the LDS becomes the merge area
-  float* mls = reinterpret_cast<float*>(smem + KW * ROWS * OSTR);  // [row][wave] (m, l)
+  float* mls = reinterpret_cast<float*>(smem + MLS_OFF);  // [row][wave] (m, l)
   {
-    uint8_t* ob = smem + wave * ROWS * OSTR;
 #pragma unroll
     for (int t = 0; t < QT; ++t) {
       const int rl = 16 * t + col;
 #pragma unroll
       for (int dt = 0; dt < G::DT; ++dt) {
         const int d = 16 * dt + 4 * grp;
-        if (d < D) *reinterpret_cast<f32x4_t*>(ob + rl * OSTR + d * 4) = oacc[dt][t];
+        if (d < D) *reinterpret_cast<f32x4_t*>(kbuf + o_chunk(rl, d / 4)) = oacc[dt][t];
       }
       if (grp == 0) *reinterpret_cast<u32x2_t*>(mls + 2 * (rl * KW + wave)) =
           u32x2_t{__float_as_uint(m_run[t]), __float_as_uint(l_tot[t])};
     }
   }
-  __syncthreads();
+  __syncthreads();  // every wave's O and (m, l) are in LDS
   constexpr int TPR = KW * 64 / ROWS;  // threads per row
   static_assert(TPR * ROWS == KW * 64, "whole rows per workgroup pass");
   const int rl = tid / TPR, c0 = tid - rl * TPR;
   const int r = row0 + rl;
   if (r < Mp) {
+    // Every LDS read of this thread is issued before any arithmetic: the
+    // (m, l) pairs of the row and the KW partial chunks (a chain of dependent
+    // read-then-multiply steps would keep only one or two reads in flight).
+    constexpr int NJ = (G::CPR + TPR - 1) / TPR;
+    f32x4_t part[NJ][KW][2];
     float mw[KW], fw[KW];
-    float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < KW; ++w) {
-      mw[w] = mls[2 * (rl * KW + w)];
-      fw[w] = mls[2 * (rl * KW + w) + 1];  // l of wave w
-      if (fw[w] > 0.f) M = fmaxf(M, mw[w]);
+      const u32x2_t ml = *reinterpret_cast<const u32x2_t*>(mls + 2 * (rl * KW + w));
+      mw[w] = __uint_as_float(ml[0]);
+      fw[w] = __uint_as_float(ml[1]);  // l of wave w
     }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int ch = min(c0 + TPR * j, G::CPR - 1);  // (a clamped chunk is read but not used)
+#pragma unroll
+      for (int w = 0; w < KW; ++w) {
+        const uint8_t* src = smem + w * WAVE_B;
+        part[j][w][0] = *reinterpret_cast<const f32x4_t*>(src + o_chunk(rl, 2 * ch));
+        part[j][w][1] = *reinterpret_cast<const f32x4_t*>(src + o_chunk(rl, 2 * ch + 1));
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < KW; ++w)
+      if (fw[w] > 0.f) M = fmaxf(M, mw[w]);
     float L = 0.f;
 #pragma unroll
     for (int w = 0; w < KW; ++w) {
@@ -853,15 +882,14 @@ fwd_ks_kernel(const FwdParams p) {
     for (int w = 0; w < KW; ++w) fw[w] *= inv;
     const int s = r / g, hh = r - s * g;
 #pragma unroll
-    for (int j = 0; j < (G::CPR + TPR - 1) / TPR; ++j) {
+    for (int j = 0; j < NJ; ++j) {
       const int ch = c0 + TPR * j;
       if (ch < G::CPR) {
         f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int w = 0; w < KW; ++w) {
-          const uint8_t* src = smem + (w * ROWS + rl) * OSTR + ch * 32;
-          a0 += fw[w] * *reinterpret_cast<const f32x4_t*>(src);
-          a1 += fw[w] * *reinterpret_cast<const f32x4_t*>(src + 16);
+          a0 += fw[w] * part[j][w][0];
+          a1 += fw[w] * part[j][w][1];
         }
         if constexpr (!SPLIT && OUTF == kOutNvfp4) {
           // chunks ch and ch ^ 1 form a block of 16; the other one is in the
