@@ -386,6 +386,7 @@ int run(const Plan& pl, const void* q, const void* k, const void* v, void* out, 
   p.Hq = Hq;
   p.Hkv = Hkv;
   p.g = Hq / Hkv;
+  p.g_m = 0xffffffffu / (uint32_t)p.g;
   p.Mp = pl.Mp;
   p.coff = Sk - Sq;
   p.lse_hs = Sq;

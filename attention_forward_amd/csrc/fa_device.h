@@ -451,8 +451,9 @@ __device__ __forceinline__ void pv_tile(f32x4_t (&oacc)[G::DT][QT], const uint32
 // n / d for 0 <= n < 2^31 and d >= 1, given m = floor((2^32 - 1) / d): the
 // high half of n*m is the quotient or one less (m > (2^32 - 1) / d - 1 and
 // n < 2^31 keep the error of n*m / 2^32 below one), so one correction step
-// makes it exact.  Scalar multiplies only, where the compiler's division
-// would go through a vector reciprocal and back.
+// makes it exact.  A multiply and a correction (scalar for uniform
+// operands, vector otherwise), where the compiler's division by a runtime
+// value takes a float reciprocal and about 30 more instructions.
 __device__ __forceinline__ int udiv(int n, int d, uint32_t m) {
   const uint32_t q = __umulhi((uint32_t)n, m);
   return (int)(q + ((uint32_t)n - q * (uint32_t)d >= (uint32_t)d ? 1u : 0u));
@@ -630,6 +631,13 @@ __host__ __device__ __forceinline__ int causal_kmax(int rb, int rows, int Mp, in
   return k < 0 ? 0 : (k > Sk ? Sk : k);
 }
 
+// causal_kmax on the device, for launch parameters p (p.Mp >= 1).
+__device__ __forceinline__ int causal_kmax_dev(const FwdParams& p, int rb, int rows) {
+  const int last_row = min((rb + 1) * rows, p.Mp) - 1;
+  const int k = udiv(last_row, p.g, p.g_m) + p.coff + 1;
+  return k < 0 ? 0 : (k > p.Sk ? p.Sk : k);
+}
+
 // Causal grids: workgroup x takes row block nrb - 1 - x / zmax (heaviest
 // first) and key range x % zmax of it (zmax = 1 without splitting).  Returns
 // false for a key range past the block's last planned key: such a workgroup
@@ -638,10 +646,10 @@ template <bool SPLIT>
 __device__ __forceinline__ bool causal_item(const FwdParams& p, int rows, int g, int& rb, int& z, int& kmax) {
   const int nrb = (p.Mp + rows - 1) / rows;
   const int x = blockIdx.x;
-  const int q = SPLIT ? x / p.zmax : x;
+  const int q = SPLIT ? udiv(x, p.zmax, p.zmax_m) : x;
   rb = nrb - 1 - q;
   z = SPLIT ? x - q * p.zmax : 0;
-  kmax = causal_kmax(rb, rows, p.Mp, g, p.coff, p.Sk);
+  kmax = causal_kmax_dev(p, rb, rows);
   return !SPLIT || z * p.kps < kmax;
 }
 
@@ -665,7 +673,10 @@ struct Seq {
   long long lse0;   // lse index of (head 0, query 0); heads are p.lse_hs apart
 };
 
-__device__ __forceinline__ Seq seq_of(const FwdParams& p, int b) {
+// With read_seqused false the fixed-shape path leaves nk at Sk and the
+// caller reads seqused_k later (seqused_count), after issuing work that
+// does not depend on it.
+__device__ __forceinline__ Seq seq_of(const FwdParams& p, int b, bool read_seqused = true) {
   Seq r;
   r.q0 = 0;
   r.sq = p.Sq;
@@ -681,7 +692,7 @@ __device__ __forceinline__ Seq seq_of(const FwdParams& p, int b) {
     e = min(max(p.cu_k[b + 1], a), p.total_k);
     r.k0 = a;
     r.nk = min(e - a, p.Sk);
-  } else if (p.seqused != nullptr) {
+  } else if (read_seqused && p.seqused != nullptr) {
     r.nk = min(max(p.seqused[b], 0), p.Sk);
   }
   // uniform per workgroup: keeps buffer resources and loop bounds scalar
@@ -691,6 +702,14 @@ __device__ __forceinline__ Seq seq_of(const FwdParams& p, int b) {
   r.nk = __builtin_amdgcn_readfirstlane(r.nk);
   r.lse0 = (long long)b * p.lse_bs + r.q0;  // one of the two terms is zero
   return r;
+}
+
+// Attended key count of batch entry b for a Seq taken with read_seqused
+// false: seqused_k[b] clamped to [0, Sk] for a fixed-shape call with a
+// seqused_k array, else the count seq_of already holds.
+__device__ __forceinline__ int seqused_count(const FwdParams& p, int b, const Seq& sq) {
+  if (p.cu_q != nullptr || p.seqused == nullptr) return sq.nk;
+  return __builtin_amdgcn_readfirstlane(min(max(p.seqused[b], 0), p.Sk));
 }
 
 struct RowBlock {

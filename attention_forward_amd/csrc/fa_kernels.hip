@@ -133,7 +133,7 @@ fwd_kernel(const FwdParams p) {
     blk.kbeg = SPLIT ? item * p.kps : 0;
     blk.kend = SPLIT ? min(blk.kbeg + p.kps, kmax) : kmax;
     // the valid keys, up to the diagonal of the block's last row
-    blk.kend = min(min(blk.kend, nvalid), (min((rb + 1) * G::ROWS_WG, Mp) - 1) / g + (nvalid - sq.sq) + 1);
+    blk.kend = min(min(blk.kend, nvalid), udiv(max(min((rb + 1) * G::ROWS_WG, Mp) - 1, 0), g, p.g_m) + (nvalid - sq.sq) + 1);
   } else {
     blk.rb = rb_x;
     blk.z = SPLIT ? blockIdx.z : 0;
@@ -151,8 +151,8 @@ fwd_kernel(const FwdParams p) {
   // Causal: diagonal keys (last attended key) of the wave's first and last
   // rows; the last query lines up with the last valid key.
   const int doff = CAUSAL ? nvalid - sq.sq : 0;
-  const int s_lo = min(rw0, Mp - 1) / g + doff;
-  const int s_hi = (min(rw0 + 16 * QT, Mp) - 1) / g + doff;
+  const int s_lo = udiv(min(rw0, Mp - 1), g, p.g_m) + doff;
+  const int s_hi = udiv(min(rw0 + 16 * QT, Mp) - 1, g, p.g_m) + doff;
 
   f32x4_t oacc[G::DT][QT];
 #pragma unroll
@@ -245,7 +245,7 @@ fwd_kernel(const FwdParams p) {
   for (int t = 0; t < QT; ++t) {
     const int r = rw0 + 16 * t + col;
     const bool ok = r < Mp;
-    const int s = ok ? r / g : 0;
+    const int s = ok ? udiv(r, g, p.g_m) : 0;
     const int hh = ok ? r - s * g : 0;
     srow[t] = ok ? s + doff : -1;  // causal: the row's diagonal key
     const uint16_t* qp = p.q + view_off(b, sq.q0 + s, hk * g + hh, p.q_sb, p.q_ss, p.q_sh);
@@ -369,7 +369,7 @@ fwd_kernel(const FwdParams p) {
     for (int t = 0; t < QT; ++t) {
       const int r = rw0 + 16 * t + col;
       if (r >= Mp) continue;
-      const int s = r / g, hh = r - s * g;
+      const int s = udiv(r, g, p.g_m), hh = r - s * g;
       const float l = l_tot[t];
       const float inv = (l > 0.f) ? 1.0f / l : 0.f;
       if constexpr (OUTF == kOutNvfp4) {
@@ -509,31 +509,61 @@ fwd_ks_kernel(const FwdParams p) {
   const int b = udiv(bh, p.Hkv, p.hkv_m), hk = bh - b * p.Hkv;
   const int g = p.g;
 
-  const Seq sq = seq_of(p, b);
-  const int nvalid = sq.nk;
+  const Seq sq = seq_of(p, b, false);
   const int Mp = sq.sq * g;  // packed rows of this batch entry (the grid covers the planned maximum)
 
   RowBlock blk;
+  int kmax = 0;
   if constexpr (CAUSAL) {
-    int rb, item, kmax;
+    int rb, item;
     if (!causal_item<SPLIT>(p, ROWS, g, rb, item, kmax)) return;
     blk.rb = rb;
     blk.z = item;
-    blk.kbeg = SPLIT ? item * p.kps : 0;
-    blk.kend = SPLIT ? min(blk.kbeg + p.kps, kmax) : kmax;
-    // the valid keys, up to the diagonal of the block's last row
-    blk.kend = min(min(blk.kend, nvalid), (min((rb + 1) * ROWS, Mp) - 1) / g + (nvalid - sq.sq) + 1);
   } else {
     blk.rb = rb_nc;
     blk.z = z_nc;
-    blk.kbeg = SPLIT ? blk.z * p.kps : 0;
-    blk.kend = SPLIT ? min(blk.kbeg + p.kps, nvalid) : nvalid;
   }
   const int row0 = blk.rb * ROWS;
   if (row0 >= Mp) return;  // past a shorter sequence of a packed batch: nothing to do
+
+  // Q tile: packed rows row0 .. row0+ROWS-1, copied once per workgroup
+  // (wave w issues copies w, w+KW, ...) into LDS at the K row stride.  The
+  // buffer starts at the block's first position; rows past Mp and the row
+  // padding read as zeros.
+  {
+    const int s_first = udiv(row0, g, p.g_m);
+    const int s_last = udiv(min(row0 + ROWS, Mp) - 1, g, p.g_m);
+    const uint32_t qrow_b = (uint32_t)(p.q_ss * 2), qhead_b = (uint32_t)(p.q_sh * 2);
+    const u32x4_t rq = make_rsrc(p.q + view_off(b, sq.q0 + s_first, hk * g, p.q_sb, p.q_ss, p.q_sh),
+                                 (uint32_t)(s_last - s_first) * qrow_b + (uint32_t)(g - 1) * qhead_b + D * 2);
+    const uint32_t lds_q = (uint32_t)(uintptr_t)(lds_void_t*)(smem + Q_OFF);
+    for (int j = wave; j < Q_INSTR; j += KW) {
+      const int P = j * 64 + lane;
+      const int row = P / (G::KSTR / 16), ch = P - row * (G::KSTR / 16);
+      const int r = row0 + row;
+      uint32_t off = kOutOfRange;
+      if (row < ROWS && ch < G::CPR && r < Mp) {
+        const int sq = udiv(r, g, p.g_m);
+        off = (uint32_t)(sq - s_first) * qrow_b + (uint32_t)(r - sq * g) * qhead_b + (uint32_t)(ch * 16);
+      }
+      copy16_to_lds(rq, off, __builtin_amdgcn_readfirstlane(lds_q + j * 1024));
+    }
+  }
+  // The valid key count (device-side seqused_k) is used only from here on,
+  // so its load completes under the Q copies.
+  __builtin_amdgcn_sched_barrier(0);
+  const int nvalid = seqused_count(p, b, sq);
+  blk.kbeg = SPLIT ? blk.z * p.kps : 0;
+  if constexpr (CAUSAL) {
+    blk.kend = SPLIT ? min(blk.kbeg + p.kps, kmax) : kmax;
+    // the valid keys, up to the diagonal of the block's last row
+    blk.kend = min(min(blk.kend, nvalid), udiv(min((blk.rb + 1) * ROWS, Mp) - 1, g, p.g_m) + (nvalid - sq.sq) + 1);
+  } else {
+    blk.kend = SPLIT ? min(blk.kbeg + p.kps, nvalid) : nvalid;
+  }
   const int kbeg = blk.kbeg, kend = blk.kend;
   const int doff = CAUSAL ? nvalid - sq.sq : 0;  // causal: diagonal key offset (last query <-> last valid key)
-  const int s_lo = min(row0, Mp - 1) / g + doff;
+  const int s_lo = udiv(min(row0, Mp - 1), g, p.g_m) + doff;
 
   typename G::E::v8 qf[QT][G::KC];
   int srow[QT];
@@ -590,29 +620,6 @@ fwd_ks_kernel(const FwdParams p) {
   const int ntiles = kend > kbeg ? (kend - kbeg + BN - 1) / BN : 0;
   const int nown = ntiles > wave ? (ntiles - wave + KW - 1) / KW : 0;  // this wave's tiles
 
-  // Q tile: packed rows row0 .. row0+ROWS-1, copied once per workgroup
-  // (wave w issues copies w, w+KW, ...) into LDS at the K row stride.  The
-  // buffer starts at the block's first position; rows past Mp and the row
-  // padding read as zeros.
-  {
-    const int s_first = row0 / g;
-    const int s_last = (min(row0 + ROWS, Mp) - 1) / g;
-    const uint32_t qrow_b = (uint32_t)(p.q_ss * 2), qhead_b = (uint32_t)(p.q_sh * 2);
-    const u32x4_t rq = make_rsrc(p.q + view_off(b, sq.q0 + s_first, hk * g, p.q_sb, p.q_ss, p.q_sh),
-                                 (uint32_t)(s_last - s_first) * qrow_b + (uint32_t)(g - 1) * qhead_b + D * 2);
-    const uint32_t lds_q = (uint32_t)(uintptr_t)(lds_void_t*)(smem + Q_OFF);
-    for (int j = wave; j < Q_INSTR; j += KW) {
-      const int P = j * 64 + lane;
-      const int row = P / (G::KSTR / 16), ch = P - row * (G::KSTR / 16);
-      const int r = row0 + row;
-      uint32_t off = kOutOfRange;
-      if (row < ROWS && ch < G::CPR && r < Mp) {
-        const int sq = r / g;
-        off = (uint32_t)(sq - s_first) * qrow_b + (uint32_t)(r - sq * g) * qhead_b + (uint32_t)(ch * 16);
-      }
-      copy16_to_lds(rq, off, __builtin_amdgcn_readfirstlane(lds_q + j * 1024));
-    }
-  }
   // Piecewise refill: lane l of a piece copy fills quarter slot l % 4 of
   // key l / 4 of its 16 keys (with the quarter swizzles above).  `toff` is
   // the tile's byte offset in the buffer range, or kOutOfRange (past the
@@ -655,7 +662,7 @@ fwd_ks_kernel(const FwdParams p) {
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
     const int r = row0 + 16 * t + col;
-    srow[t] = r < Mp ? r / g + doff : -1;  // causal: the row's diagonal key
+    srow[t] = r < Mp ? udiv(r, g, p.g_m) + doff : -1;  // causal: the row's diagonal key
 #pragma unroll
     for (int c = 0; c < G::KC; ++c) {
       qf[t][c] = G::E::cast(*reinterpret_cast<const u32x4_t*>(smem + Q_OFF + (16 * t + col) * G::KSTR + c * 64 + grp * 16));
@@ -880,7 +887,7 @@ fwd_ks_kernel(const FwdParams p) {
     const float inv = (L > 0.f) ? 1.0f / L : 0.f;
 #pragma unroll
     for (int w = 0; w < KW; ++w) fw[w] *= inv;
-    const int s = r / g, hh = r - s * g;
+    const int s = udiv(r, g, p.g_m), hh = r - s * g;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int ch = c0 + TPR * j;
@@ -950,7 +957,7 @@ combine_kernel(const FwdParams p) {
   if (r >= sq.sq * g) return;  // past the end of this batch entry's queries
   int nz = p.zmax;
   if constexpr (CAUSAL) {
-    nz = (causal_kmax(rb, ROWS_WG, p.Mp, g, p.coff, p.Sk) + p.kps - 1) / p.kps;
+    nz = (causal_kmax_dev(p, rb, ROWS_WG) + p.kps - 1) / p.kps;
   }
   const size_t slot_base = ((size_t)bh * p.nrb + rb) * p.zmax;
   float M = -INFINITY, L = 0.f;
@@ -979,7 +986,7 @@ combine_kernel(const FwdParams p) {
       M = m_new;
     }
   }
-  const int s = r / g, hh = r - s * g;
+  const int s = udiv(r, g, p.g_m), hh = r - s * g;
   const float inv = (L > 0.f) ? 1.0f / L : 0.f;
   if constexpr (OUTF == kOutNvfp4) {
     // a block of 16 is chunks 4j .. 4j+3, held by threads i with the same

@@ -33,6 +33,7 @@ struct FwdParams {
   float* ws_ml;            // partial (m in log2 units, l), fp32 pairs
   int B, Sq, Sk, Hq, Hkv;
   int g;                   // Hq / Hkv
+  uint32_t g_m;            // floor((2^32 - 1) / g), multiplier for udiv
   int Mp;                  // packed rows per (batch, kv head) = Sq * g
   int coff;                // Sk - Sq: causal diagonal offset of the full key buffer (grid planning)
   int kps;                 // keys per split (multiple of the key tile), split variants only
