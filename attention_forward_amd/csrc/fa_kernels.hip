@@ -696,7 +696,9 @@ fwd_ks_kernel(const FwdParams p) {
     // reads): WK.  Likewise WV before a V read.  The first tile differs: its
     // V pieces are issued during its own S^T (step c: V(0) piece c, then
     // K(1) piece c), so that the S^T MFMAs overlap them; its counts follow
-    // that order (k_wait, v_wait below, exact per read).
+    // that order (k_wait, v_wait below, exact per read).  The last tile of a
+    // wave issues no copies, so only the pieces of its own tile (and, in the
+    // first tile, its V pieces) can follow a piece it reads.
     constexpr int PF = 3;   // K steps whose fragments are read ahead of their MFMAs
     constexpr int PFV = 6;  // V fragments read ahead
     constexpr int WK = 2 * (G::KC - 1) + 2 * V_PIECES - 2 * PF;
@@ -706,13 +708,16 @@ fwd_ks_kernel(const FwdParams p) {
     static_assert(2 * V_PIECES == 2 * G::KC, "one V piece per K step of the first tile");
     // first tile: K(0) piece c' (prologue) is followed by the rest of K(0) and
     // 4 copies per S^T step issued before its read (at step c' - PF)
-    auto k_wait = [](bool first, int c_read) constexpr -> int {
-      return first ? 2 * (G::KC - 1 - c_read) + 4 * (c_read >= PF ? c_read - PF : 0) : WK;
+    auto k_wait = [](bool first, bool last, int c_read) constexpr -> int {
+      const int ahead = c_read >= PF ? c_read - PF : 0;  // S^T steps whose copies precede the read
+      if (last) return 2 * (G::KC - 1 - c_read) + (first ? 2 * ahead : 2 * V_PIECES);
+      return first ? 2 * (G::KC - 1 - c_read) + 4 * ahead : WK;
     };
     // first tile: V(0) piece e is followed by K(1) piece e, the later steps'
     // 4 copies, and the V(1) pieces issued before its read (after every
     // second O^T step)
-    auto v_wait = [](bool first, int d_read) constexpr -> int {
+    auto v_wait = [](bool first, bool last, int d_read) constexpr -> int {
+      if (last) return 2 * (V_PIECES - 1 - (d_read >> 1));
       return first ? 2 + 4 * (V_PIECES - 1 - (d_read >> 1)) + 2 * (d_read >= PFV ? (d_read - PFV) >> 1 : 0) : WV;
     };
     auto read_k = [&](int c, int mt) __attribute__((always_inline)) -> typename G::E::v8 {
@@ -726,21 +731,19 @@ fwd_ks_kernel(const FwdParams p) {
                           __builtin_bit_cast(u32x2_t, hi)[0], __builtin_bit_cast(u32x2_t, hi)[1]};
       return G::E::cast(vw);
     };
-    auto tile = [&](auto first_tag, int i) __attribute__((always_inline)) {
+    auto tile = [&](auto first_tag, auto last_tag, int i) __attribute__((always_inline)) {
       constexpr bool FIRST = decltype(first_tag)::value;
+      constexpr bool LAST = decltype(last_tag)::value;  // no next tile: no copies
       const int kt = kbeg + (wave + i * KW) * BN;
-      // the next tile of this wave, or (last tile) copies that read nothing,
-      // which keep the wait counts of every tile the same
-      const bool next = i + 1 < nown;
-      const uint32_t tk = next ? (uint32_t)(kt + KW * BN) * rstride_k : kOutOfRange;
-      const uint32_t tv = next ? (uint32_t)(kt + KW * BN) * rstride_v : kOutOfRange;
+      const uint32_t tk = (uint32_t)(kt + KW * BN) * rstride_k;  // the next tile of this wave
+      const uint32_t tv = (uint32_t)(kt + KW * BN) * rstride_v;
       f32x4_t sacc[G::MT][QT];
 #pragma unroll
       for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
         for (int t = 0; t < QT; ++t) sacc[mt][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       typename G::E::v8 kf[G::KC][G::MT];
-      wait_vm(k_wait(FIRST, PF - 1));
+      wait_vm(k_wait(FIRST, LAST, PF - 1));
 #pragma unroll
       for (int c = 0; c < PF; ++c)
 #pragma unroll
@@ -748,7 +751,7 @@ fwd_ks_kernel(const FwdParams p) {
 #pragma unroll
       for (int c = 0; c < G::KC; ++c) {
         if (c + PF < G::KC) {
-          wait_vm(k_wait(FIRST, c + PF));
+          wait_vm(k_wait(FIRST, LAST, c + PF));
 #pragma unroll
           for (int mt = 0; mt < G::MT; ++mt) kf[c + PF][mt] = read_k(c + PF, mt);
         }
@@ -762,23 +765,25 @@ fwd_ks_kernel(const FwdParams p) {
           copy_v_piece((uint32_t)kt * rstride_v, c, 0);  // the V buffer is not read before O^T
           copy_v_piece((uint32_t)kt * rstride_v, c, 1);
         }
-        // the reads of step c have returned (fewer than 2 PF reads issued since)
-        wait_lgkm(2 * (G::KC - 1 - c < PF ? G::KC - 1 - c : PF));
+        if constexpr (!LAST) {
+          // the reads of step c have returned (fewer than 2 PF reads issued since)
+          wait_lgkm(2 * (G::KC - 1 - c < PF ? G::KC - 1 - c : PF));
 #pragma unroll
-        for (int mt = 0; mt < G::MT; ++mt) copy_k_piece(tk, c, mt);
+          for (int mt = 0; mt < G::MT; ++mt) copy_k_piece(tk, c, mt);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
       uint32_t pk[G::KVC][QT][4];
       softmax_tile<G, QT, CAUSAL>(sacc, pk, m_run, l_run, oacc, srow, kt, kend, s_lo, c2, grp);
       __builtin_amdgcn_sched_barrier(0);
       typename G::E::v8 vf[G::DT];
-      wait_vm(v_wait(FIRST, PFV - 1));
+      wait_vm(v_wait(FIRST, LAST, PFV - 1));
 #pragma unroll
       for (int dt = 0; dt < PFV; ++dt) vf[dt] = read_v(dt);
 #pragma unroll
       for (int dt = 0; dt < G::DT; ++dt) {
         if (dt + PFV < G::DT) {
-          wait_vm(v_wait(FIRST, dt + PFV));
+          wait_vm(v_wait(FIRST, LAST, dt + PFV));
           vf[dt + PFV] = read_v(dt + PFV);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -788,7 +793,7 @@ fwd_ks_kernel(const FwdParams p) {
           oacc[dt][t] = G::E::mfma(vf[dt], G::E::cast(pw), oacc[dt][t]);
         }
         __builtin_amdgcn_sched_barrier(0);
-        if (dt & 1) {
+        if (!LAST && (dt & 1)) {
           // both columns of piece dt/2 have been read
           wait_lgkm(2 * (G::DT - 1 - dt < PFV ? G::DT - 1 - dt : PFV));
           copy_v_piece(tv, dt >> 1, 0);
@@ -797,8 +802,13 @@ fwd_ks_kernel(const FwdParams p) {
         __builtin_amdgcn_sched_barrier(0);
       }
     };
-    if (nown > 0) tile(std::true_type{}, 0);
-    for (int i = 1; i < nown; ++i) tile(std::false_type{}, i);
+    if (nown == 1) {
+      tile(std::true_type{}, std::true_type{}, 0);
+    } else if (nown > 1) {
+      tile(std::true_type{}, std::false_type{}, 0);
+      for (int i = 1; i < nown - 1; ++i) tile(std::false_type{}, std::false_type{}, i);
+      tile(std::false_type{}, std::true_type{}, nown - 1);
+    }
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the last copies have landed before the LDS is reused
   } else
   for (int i = 0; i < nown; ++i) {
