@@ -474,10 +474,10 @@ fwd_ks_kernel(const FwdParams p) {
   constexpr int Q_INSTR = round_up(ROWS * (G::KSTR / 16), 64) / 64;  // 1 KiB copies of the Q tile
   constexpr int Q_OFF = KW * WAVE_B;
   // Merge area: wave w's O rows go into its own K/V buffer, so a wave
-  // stores them as soon as its own tiles are done.  Rows of a power-of-two
+  // stores them as soon as its own tiles are done.  Rows that are a whole
   // number of 256-byte bank rows are unpadded, their 16-byte chunks
-  // XOR-swizzled by the row (chunk c of row r at c ^ (r % 16)); others are
-  // padded by 16 bytes.  Either way the 16 rows one store instruction
+  // XOR-swizzled by the row (chunk c of row r at c ^ (r % 16), which stays
+  // inside c's group of 16 chunks); others are padded by 16 bytes.  Either way the 16 rows one store instruction
   // covers, and the rows and chunks one merge read covers, fall in
   // different banks.
   constexpr bool OSWZ = (D * 4) % 256 == 0;
