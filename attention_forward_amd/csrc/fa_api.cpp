@@ -176,14 +176,25 @@ Plan default_plan(int B, int Sq, int Sk, int Hq, int Hkv, int D, int causal) {
     pl.launch.bn = 32;
     pl.launch.nst = 2;
   } else if (D == 256 && !causal && pl.kps == 0 && base > kTargetWorkgroups) {
-    // Two or three rounds: row-split blocks of four 16-row waves over 64-key
-    // tiles (2 x 768 x 768 prefix rows: 27.5 -> 25.6 us; 2 x 1024 x 1024:
-    // 34.5 -> 32.8 us).
-    pl.launch.qt = 1;
-    pl.launch.nw = 4;
-    pl.launch.kw = 1;
-    pl.launch.bn = 64;
-    pl.launch.nst = 2;
+    // Two or three rounds: the key-split kernel's ring buffer scheme, two
+    // workgroups per compute unit.  Measured against row-split blocks of
+    // four 16-row waves over 64-key tiles and against the two-buffer
+    // key-split kernel (us per call): 2 x 768 x 768 prefix rows 25.2 / 21.5
+    // -> 19.7; 2 x 1024 x 1024 32.3 / 27.2 -> 27.0; 3 x 1024 x 1024 62.9 /
+    // 45.1 -> 41.9; 3 x 700 x 700 45.5 / 30.3 -> 27.9; 1536 x 1536 44.8 /
+    // 34.5 -> 32.6; 1024 x 1024 with 16/2 heads 32.8 / 27.3 -> 27.2.
+    pl.launch.nst = 3;
+  }
+  if (D == 256 && causal && pl.kps == 0 && pl.launch.kw == 4 && BH == 1 &&
+      base > 2 * kTargetWorkgroups - kTargetWorkgroups / 8 && base <= 2 * kTargetWorkgroups) {
+    // Causal grids of one (batch, kv head) with about two row blocks per
+    // compute unit: the ring buffer scheme (80 KiB of LDS, two waves per
+    // SIMD) with a heavy and a light row block on each compute unit, so
+    // that one workgroup's prologue and merge overlap the other's tiles
+    // (causal 2048 prefill 28.4 -> 27.2 us).  With fewer blocks the
+    // heaviest ones run alone on their compute units, where the ring's
+    // half-size buffers are slower (384 blocks: 19.7 -> 21.9 us).
+    pl.launch.nst = 3;
   }
   if (D != 256 && pl.kps == 0) {
     // Single-pass row-split grids: two key groups of waves on the same rows

@@ -642,11 +642,24 @@ __device__ __forceinline__ int causal_kmax_dev(const FwdParams& p, int rb, int r
 // first) and key range x % zmax of it (zmax = 1 without splitting).  Returns
 // false for a key range past the block's last planned key: such a workgroup
 // has no work, and the merge reads no partial from it.
-template <bool SPLIT>
+// PAIRED (unsplit grids of one (batch, kv head) whose workgroups are all
+// resident at once, two per compute unit): the first half of the grid takes the heavy blocks from the
+// heaviest down, the second half the light ones from the lightest up, so
+// workgroups x and x + nrb/2, which the dispatcher places in the same order
+// over the compute units, together attend about the same number of keys on
+// every compute unit.
+template <bool SPLIT, bool PAIRED = false>
 __device__ __forceinline__ bool causal_item(const FwdParams& p, int rows, int g, int& rb, int& z, int& kmax) {
   const int nrb = (p.Mp + rows - 1) / rows;
   const int x = blockIdx.x;
-  const int q = SPLIT ? udiv(x, p.zmax, p.zmax_m) : x;
+  int q = SPLIT ? udiv(x, p.zmax, p.zmax_m) : x;
+  if constexpr (PAIRED && !SPLIT) {
+    // (one (batch, kv head) and at most two workgroups per compute unit)
+    if (gridDim.y == 1 && nrb <= 2 * kComputeUnits) {
+      const int half = (nrb + 1) >> 1;
+      if (x >= half) q = nrb - 1 - (x - half);
+    }
+  }
   rb = nrb - 1 - q;
   z = SPLIT ? x - q * p.zmax : 0;
   kmax = causal_kmax_dev(p, rb, rows);

@@ -457,21 +457,26 @@ fwd_kernel(const FwdParams p) {
 // Copies of 64-byte row segments run at the full intake rate (32-byte
 // segments at about half).
 template <int D, int QT, int KW, int BN, int NST, bool CAUSAL, bool SPLIT, int DTY, int OUTF>
-__global__ void __launch_bounds__(KW * 64, 1)
+__global__ void __launch_bounds__(KW * 64, NST == 3 ? 2 : 1)
 fwd_ks_kernel(const FwdParams p) {
   using G = Geo<D, QT, 1, BN, DTY>;  // per-wave geometry: one wave issues its own tile copies
   constexpr int ROWS = 16 * QT;
-  constexpr bool PIECES = NST == 2;
+  constexpr bool PIECES = NST >= 2;
+  constexpr bool RING = NST == 3;
   pin_params(p);
-  static_assert(NST == 1 || NST == 2, "buffer scheme");
+  static_assert(NST >= 1 && NST <= 3, "buffer scheme");
   static_assert(!G::TRASH, "per-wave tiles must be whole 64-slot windows");
   static_assert(!PIECES || (BN == 32 && D % 32 == 0), "piecewise refill: 32-key tiles, whole 32-element K steps");
+  static_assert(!RING || (D == 256 && QT == 2), "ring: 32 rows of head dim 256");
   // LDS: KW per-wave K/V buffers, then the workgroup's Q tile (rows at the K
-  // stride, read like K fragments); after the main loop the same memory is
+  // stride, read like K fragments; in the ring scheme unpadded, its 16-byte
+  // chunks XOR-swizzled by the row); after the main loop the same memory is
   // the merge area.
   constexpr int K_PIECES = G::KC * G::MT, V_PIECES = G::DT / 2;  // 1 KiB K pieces, 2 KiB V pieces
-  constexpr int WAVE_B = PIECES ? (K_PIECES + 2 * V_PIECES) * 1024 : G::STAGE_B;
-  constexpr int Q_INSTR = round_up(ROWS * (G::KSTR / 16), 64) / 64;  // 1 KiB copies of the Q tile
+  constexpr int WAVE_B = RING ? K_PIECES * 1024 : PIECES ? (K_PIECES + 2 * V_PIECES) * 1024 : G::STAGE_B;
+  static_assert(!RING || K_PIECES == 2 * V_PIECES, "a ring slot holds either two K pieces or one V piece");
+  constexpr int QSTR = RING ? D * 2 : G::KSTR;                     // Q row stride in LDS
+  constexpr int Q_INSTR = round_up(ROWS * (QSTR / 16), 64) / 64;  // 1 KiB copies of the Q tile
   constexpr int Q_OFF = KW * WAVE_B;
   // Merge area: wave w's O rows go into its own K/V buffer, so a wave
   // stores them as soon as its own tiles are done.  Rows that are a whole
@@ -482,10 +487,14 @@ fwd_ks_kernel(const FwdParams p) {
   // different banks.
   constexpr bool OSWZ = (D * 4) % 256 == 0;
   constexpr int OSTR = OSWZ ? D * 4 : D * 4 + 16;
-  static_assert(ROWS * OSTR <= WAVE_B, "a wave's O rows fit its K/V buffer");
-  constexpr int MLS_OFF = Q_OFF + Q_INSTR * 1024;  // (m, l) per row and wave
-  constexpr int LDS_B = MLS_OFF + KW * ROWS * 8;
-  static_assert(LDS_B <= 160 * 1024, "LDS of one workgroup");
+  constexpr int OROWS = RING ? 16 : ROWS;  // O rows a wave stores per merge pass
+  static_assert(OROWS * OSTR <= WAVE_B, "a wave's O rows of one merge pass fit its K/V buffer");
+  // (m, l) per row and wave; in the ring scheme in the Q area, which is
+  // free once every wave has read its Q fragments
+  constexpr int MLS_OFF = RING ? Q_OFF : Q_OFF + Q_INSTR * 1024;
+  constexpr int LDS_B = RING ? Q_OFF + Q_INSTR * 1024 : MLS_OFF + KW * ROWS * 8;
+  static_assert(!RING || KW * ROWS * 8 <= Q_INSTR * 1024, "ring: (m, l) fit the Q area");
+  static_assert(LDS_B <= (RING ? 80 : 160) * 1024, "LDS of one workgroup (ring: two per compute unit)");
   __shared__ __attribute__((aligned(16))) uint8_t smem[LDS_B];
 
   const int tid = threadIdx.x;
@@ -516,7 +525,7 @@ fwd_ks_kernel(const FwdParams p) {
   int kmax = 0;
   if constexpr (CAUSAL) {
     int rb, item;
-    if (!causal_item<SPLIT>(p, ROWS, g, rb, item, kmax)) return;
+    if (!causal_item<SPLIT, RING>(p, ROWS, g, rb, item, kmax)) return;
     blk.rb = rb;
     blk.z = item;
   } else {
@@ -539,7 +548,8 @@ fwd_ks_kernel(const FwdParams p) {
     const uint32_t lds_q = (uint32_t)(uintptr_t)(lds_void_t*)(smem + Q_OFF);
     for (int j = wave; j < Q_INSTR; j += KW) {
       const int P = j * 64 + lane;
-      const int row = P / (G::KSTR / 16), ch = P - row * (G::KSTR / 16);
+      const int row = P / (QSTR / 16), sc = P - row * (QSTR / 16);
+      const int ch = RING ? (sc ^ (row & 15)) : sc;  // the chunk this LDS slot holds
       const int r = row0 + row;
       uint32_t off = kOutOfRange;
       if (row < ROWS && ch < G::CPR && r < Mp) {
@@ -598,7 +608,7 @@ fwd_ks_kernel(const FwdParams p) {
     voff_v[j] = (ch < G::CPR) ? row * rstride_v + ch * 16 : kOutOfRange;
   }
   uint8_t* kbuf = smem + wave * WAVE_B;
-  uint8_t* vbuf = kbuf + (PIECES ? K_PIECES * 1024 : G::K_B);
+  uint8_t* vbuf = RING ? kbuf : kbuf + (PIECES ? K_PIECES * 1024 : G::K_B);
   const uint32_t lds_k = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)kbuf);
   const uint32_t lds_v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)vbuf);
   // A buffer is refilled only after this wave's reads of it have returned.
@@ -665,7 +675,8 @@ fwd_ks_kernel(const FwdParams p) {
     srow[t] = r < Mp ? udiv(r, g, p.g_m) + doff : -1;  // causal: the row's diagonal key
 #pragma unroll
     for (int c = 0; c < G::KC; ++c) {
-      qf[t][c] = G::E::cast(*reinterpret_cast<const u32x4_t*>(smem + Q_OFF + (16 * t + col) * G::KSTR + c * 64 + grp * 16));
+      const int qch = RING ? ((4 * c + grp) ^ col) : 4 * c + grp;  // row 16t + col: swizzle by col
+      qf[t][c] = G::E::cast(*reinterpret_cast<const u32x4_t*>(smem + Q_OFF + (16 * t + col) * QSTR + qch * 16));
     }
   }
 
@@ -699,8 +710,19 @@ fwd_ks_kernel(const FwdParams p) {
     // that order (k_wait, v_wait below, exact per read).  The last tile of a
     // wave issues no copies, so only the pieces of its own tile (and, in the
     // first tile, its V pieces) can follow a piece it reads.
-    constexpr int PF = 3;   // K steps whose fragments are read ahead of their MFMAs
-    constexpr int PFV = 6;  // V fragments read ahead
+    //
+    // Ring scheme (two workgroups per compute unit, two waves per SIMD): a
+    // wave has one 16 KiB buffer of KC slots of 2 KiB.  Slot c holds K
+    // pieces (c, 0) and (c, 1) during S^T, then V piece c during O^T: in S^T
+    // step c, once the reads of K slot c have returned, V(i) piece c is
+    // issued into it, and in O^T, once both columns of V piece c have been
+    // read, K(i+1) pieces (c, *) are.  Every tile (the first included, whose
+    // K pieces the prologue issues) then sees the same order: before a K
+    // read of tile i come only the later K(i) pieces and the V(i) pieces of
+    // the earlier S^T steps; before a V read, the later V(i) pieces and the
+    // K(i+1) pieces of the earlier O^T steps (none in a wave's last tile).
+    constexpr int PF = RING ? 1 : 3;   // K steps whose fragments are read ahead of their MFMAs
+    constexpr int PFV = RING ? 4 : 6;  // V fragments read ahead
     constexpr int WK = 2 * (G::KC - 1) + 2 * V_PIECES - 2 * PF;
     constexpr int WV = 2 * (V_PIECES - 1) + K_PIECES - PFV;
     static_assert(PFV % 2 == 0, "V reads run ahead by whole pieces");
@@ -710,6 +732,7 @@ fwd_ks_kernel(const FwdParams p) {
     // 4 copies per S^T step issued before its read (at step c' - PF)
     auto k_wait = [](bool first, bool last, int c_read) constexpr -> int {
       const int ahead = c_read >= PF ? c_read - PF : 0;  // S^T steps whose copies precede the read
+      if (RING) return 2 * (G::KC - 1 - c_read) + 2 * ahead;
       if (last) return 2 * (G::KC - 1 - c_read) + (first ? 2 * ahead : 2 * V_PIECES);
       return first ? 2 * (G::KC - 1 - c_read) + 4 * ahead : WK;
     };
@@ -717,6 +740,7 @@ fwd_ks_kernel(const FwdParams p) {
     // 4 copies, and the V(1) pieces issued before its read (after every
     // second O^T step)
     auto v_wait = [](bool first, bool last, int d_read) constexpr -> int {
+      if (RING) return 2 * (V_PIECES - 1 - (d_read >> 1)) + (last || d_read < PFV ? 0 : 2 * ((d_read - PFV) >> 1));
       if (last) return 2 * (V_PIECES - 1 - (d_read >> 1));
       return first ? 2 + 4 * (V_PIECES - 1 - (d_read >> 1)) + 2 * (d_read >= PFV ? (d_read - PFV) >> 1 : 0) : WV;
     };
@@ -761,11 +785,16 @@ fwd_ks_kernel(const FwdParams p) {
 #pragma unroll
           for (int t = 0; t < QT; ++t) sacc[mt][t] = G::E::mfma(kf[c][mt], qf[t][c], sacc[mt][t]);
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (FIRST) {
+        if constexpr (RING) {
+          // the reads of K slot c have returned: V(i) piece c goes into it
+          wait_lgkm(2 * (G::KC - 1 - c < PF ? G::KC - 1 - c : PF));
+          copy_v_piece((uint32_t)kt * rstride_v, c, 0);
+          copy_v_piece((uint32_t)kt * rstride_v, c, 1);
+        } else if constexpr (FIRST) {
           copy_v_piece((uint32_t)kt * rstride_v, c, 0);  // the V buffer is not read before O^T
           copy_v_piece((uint32_t)kt * rstride_v, c, 1);
         }
-        if constexpr (!LAST) {
+        if constexpr (!LAST && !RING) {
           // the reads of step c have returned (fewer than 2 PF reads issued since)
           wait_lgkm(2 * (G::KC - 1 - c < PF ? G::KC - 1 - c : PF));
 #pragma unroll
@@ -796,8 +825,13 @@ fwd_ks_kernel(const FwdParams p) {
         if (!LAST && (dt & 1)) {
           // both columns of piece dt/2 have been read
           wait_lgkm(2 * (G::DT - 1 - dt < PFV ? G::DT - 1 - dt : PFV));
-          copy_v_piece(tv, dt >> 1, 0);
-          copy_v_piece(tv, dt >> 1, 1);
+          if constexpr (RING) {
+            copy_k_piece(tk, dt >> 1, 0);
+            copy_k_piece(tk, dt >> 1, 1);
+          } else {
+            copy_v_piece(tv, dt >> 1, 0);
+            copy_v_piece(tv, dt >> 1, 1);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -841,105 +875,134 @@ fwd_ks_kernel(const FwdParams p) {
 #pragma unroll
   for (int t = 0; t < QT; ++t) l_tot[t] = group_sum(l_run[t]);
   float* mls = reinterpret_cast<float*>(smem + MLS_OFF);  // [row][wave] (m, l)
-  {
+  // Wave stores of O rows 16t .. 16t+15 at row `orow` of the wave's buffer.
+  auto store_o = [&](int t, int orow) __attribute__((always_inline)) {
+#pragma unroll
+    for (int dt = 0; dt < G::DT; ++dt) {
+      const int d = 16 * dt + 4 * grp;
+      if (d < D) *reinterpret_cast<f32x4_t*>(kbuf + o_chunk(orow, d / 4)) = oacc[dt][t];
+    }
+  };
+  auto store_ml = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < QT; ++t) {
       const int rl = 16 * t + col;
-#pragma unroll
-      for (int dt = 0; dt < G::DT; ++dt) {
-        const int d = 16 * dt + 4 * grp;
-        if (d < D) *reinterpret_cast<f32x4_t*>(kbuf + o_chunk(rl, d / 4)) = oacc[dt][t];
-      }
       if (grp == 0) *reinterpret_cast<u32x2_t*>(mls + 2 * (rl * KW + wave)) =
           u32x2_t{__float_as_uint(m_run[t]), __float_as_uint(l_tot[t])};
     }
-  }
-  __syncthreads();  // every wave's O and (m, l) are in LDS
-  constexpr int TPR = KW * 64 / ROWS;  // threads per row
-  static_assert(TPR * ROWS == KW * 64, "whole rows per workgroup pass");
-  const int rl = tid / TPR, c0 = tid - rl * TPR;
-  const int r = row0 + rl;
-  if (r < Mp) {
-    // Every LDS read of this thread is issued before any arithmetic: the
-    // (m, l) pairs of the row and the KW partial chunks (a chain of dependent
-    // read-then-multiply steps would keep only one or two reads in flight).
-    constexpr int NJ = (G::CPR + TPR - 1) / TPR;
-    f32x4_t part[NJ][KW][2];
-    float mw[KW], fw[KW];
-#pragma unroll
-    for (int w = 0; w < KW; ++w) {
-      const u32x2_t ml = *reinterpret_cast<const u32x2_t*>(mls + 2 * (rl * KW + w));
-      mw[w] = __uint_as_float(ml[0]);
-      fw[w] = __uint_as_float(ml[1]);  // l of wave w
-    }
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int ch = min(c0 + TPR * j, G::CPR - 1);  // (a clamped chunk is read but not used)
+  };
+  // Merge of block rows rfirst .. rfirst+NR-1, whose O rows sit at rows
+  // 0 .. NR-1 of every wave's buffer: TPR threads per row.
+  auto merge_rows = [&](auto nr_tag, int rfirst) __attribute__((always_inline)) {
+    constexpr int NR = decltype(nr_tag)::value;
+    constexpr int TPR = KW * 64 / NR;  // threads per row
+    static_assert(TPR * NR == KW * 64, "whole rows per workgroup pass");
+    const int rl = rfirst + tid / TPR, c0 = tid - (tid / TPR) * TPR;
+    const int orow = rl - rfirst;
+    const int r = row0 + rl;
+    if (r < Mp) {
+      // Every LDS read of this thread is issued before any arithmetic: the
+      // (m, l) pairs of the row and the KW partial chunks (a chain of dependent
+      // read-then-multiply steps would keep only one or two reads in flight).
+      constexpr int NJ = (G::CPR + TPR - 1) / TPR;
+      f32x4_t part[NJ][KW][2];
+      float mw[KW], fw[KW];
 #pragma unroll
       for (int w = 0; w < KW; ++w) {
-        const uint8_t* src = smem + w * WAVE_B;
-        part[j][w][0] = *reinterpret_cast<const f32x4_t*>(src + o_chunk(rl, 2 * ch));
-        part[j][w][1] = *reinterpret_cast<const f32x4_t*>(src + o_chunk(rl, 2 * ch + 1));
+        const u32x2_t ml = *reinterpret_cast<const u32x2_t*>(mls + 2 * (rl * KW + w));
+        mw[w] = __uint_as_float(ml[0]);
+        fw[w] = __uint_as_float(ml[1]);  // l of wave w
       }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < KW; ++w)
-      if (fw[w] > 0.f) M = fmaxf(M, mw[w]);
-    float L = 0.f;
-#pragma unroll
-    for (int w = 0; w < KW; ++w) {
-      const float e = fw[w] > 0.f ? __builtin_amdgcn_exp2f(mw[w] - M) : 0.f;
-      L += fw[w] * e;
-      fw[w] = e;
-    }
-    const float inv = (L > 0.f) ? 1.0f / L : 0.f;
-#pragma unroll
-    for (int w = 0; w < KW; ++w) fw[w] *= inv;
-    const int s = udiv(r, g, p.g_m), hh = r - s * g;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int ch = c0 + TPR * j;
-      if (ch < G::CPR) {
-        f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < NJ; ++j) {
+        const int ch = min(c0 + TPR * j, G::CPR - 1);  // (a clamped chunk is read but not used)
 #pragma unroll
         for (int w = 0; w < KW; ++w) {
-          a0 += fw[w] * part[j][w][0];
-          a1 += fw[w] * part[j][w][1];
+          const uint8_t* src = smem + w * WAVE_B;
+          part[j][w][0] = *reinterpret_cast<const f32x4_t*>(src + o_chunk(orow, 2 * ch));
+          part[j][w][1] = *reinterpret_cast<const f32x4_t*>(src + o_chunk(orow, 2 * ch + 1));
         }
-        if constexpr (!SPLIT && OUTF == kOutNvfp4) {
-          // chunks ch and ch ^ 1 form a block of 16; the other one is in the
-          // neighbouring thread (tid ^ 1: same row, TPR even)
-          float am = fmaxf(amax4(a0), amax4(a1));
-          am = fmaxf(am, __shfl_xor(am, 1));
-          float div;
-          const uint32_t sc = nvfp4_scale(am, div);
-          const size_t row = nvfp4_row(p, b, s, hk * g + hh);
-          *reinterpret_cast<uint32_t*>(p.fp4_out + row * (D / 2) + 4 * ch) =
-              nvfp4_pack4(a0, div) | (nvfp4_pack4(a1, div) << 16);
-          if ((ch & 1) == 0) p.fp4_sf[row * (D / 16) + (ch >> 1)] = (uint8_t)sc;
-        } else if constexpr (!SPLIT) {
-          const u32x4_t o = {G::E::pack(a0[0], a0[1]), G::E::pack(a0[2], a0[3]), G::E::pack(a1[0], a1[1]),
-                             G::E::pack(a1[2], a1[3])};
-          *reinterpret_cast<u32x4_t*>(p.out + view_off(b, sq.q0 + s, hk * g + hh, p.o_sb, p.o_ss, p.o_sh) + 8 * ch) = o;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < KW; ++w)
+        if (fw[w] > 0.f) M = fmaxf(M, mw[w]);
+      float L = 0.f;
+#pragma unroll
+      for (int w = 0; w < KW; ++w) {
+        const float e = fw[w] > 0.f ? __builtin_amdgcn_exp2f(mw[w] - M) : 0.f;
+        L += fw[w] * e;
+        fw[w] = e;
+      }
+      const float inv = (L > 0.f) ? 1.0f / L : 0.f;
+#pragma unroll
+      for (int w = 0; w < KW; ++w) fw[w] *= inv;
+      const int s = udiv(r, g, p.g_m), hh = r - s * g;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int ch = c0 + TPR * j;
+        if (ch < G::CPR) {
+          f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int w = 0; w < KW; ++w) {
+            a0 += fw[w] * part[j][w][0];
+            a1 += fw[w] * part[j][w][1];
+          }
+          if constexpr (!SPLIT && OUTF == kOutNvfp4) {
+            // chunks ch and ch ^ 1 form a block of 16; the other one is in the
+            // neighbouring thread (tid ^ 1: same row, TPR even)
+            float am = fmaxf(amax4(a0), amax4(a1));
+            am = fmaxf(am, __shfl_xor(am, 1));
+            float div;
+            const uint32_t sc = nvfp4_scale(am, div);
+            const size_t row = nvfp4_row(p, b, s, hk * g + hh);
+            *reinterpret_cast<uint32_t*>(p.fp4_out + row * (D / 2) + 4 * ch) =
+                nvfp4_pack4(a0, div) | (nvfp4_pack4(a1, div) << 16);
+            if ((ch & 1) == 0) p.fp4_sf[row * (D / 16) + (ch >> 1)] = (uint8_t)sc;
+          } else if constexpr (!SPLIT) {
+            const u32x4_t o = {G::E::pack(a0[0], a0[1]), G::E::pack(a0[2], a0[3]), G::E::pack(a1[0], a1[1]),
+                               G::E::pack(a1[2], a1[3])};
+            *reinterpret_cast<u32x4_t*>(p.out + view_off(b, sq.q0 + s, hk * g + hh, p.o_sb, p.o_ss, p.o_sh) + 8 * ch) = o;
+          } else {
+            const size_t prow = (((size_t)bh * p.nrb + blk.rb) * p.zmax + blk.z) * ROWS + rl;
+            float* po = p.ws_o + prow * D + 8 * ch;
+            *reinterpret_cast<f32x4_t*>(po) = a0;
+            *reinterpret_cast<f32x4_t*>(po + 4) = a1;
+          }
+        }
+      }
+      if (c0 == 0) {
+        if constexpr (!SPLIT) {
+          if (p.lse != nullptr)
+            p.lse[sq.lse0 + (long long)(hk * g + hh) * p.lse_hs + s] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : -INFINITY;
         } else {
           const size_t prow = (((size_t)bh * p.nrb + blk.rb) * p.zmax + blk.z) * ROWS + rl;
-          float* po = p.ws_o + prow * D + 8 * ch;
-          *reinterpret_cast<f32x4_t*>(po) = a0;
-          *reinterpret_cast<f32x4_t*>(po + 4) = a1;
+          *reinterpret_cast<u32x2_t*>(p.ws_ml + 2 * prow) = u32x2_t{__float_as_uint(M), __float_as_uint(L)};
         }
       }
     }
-    if (c0 == 0) {
-      if constexpr (!SPLIT) {
-        if (p.lse != nullptr)
-          p.lse[sq.lse0 + (long long)(hk * g + hh) * p.lse_hs + s] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : -INFINITY;
-      } else {
-        const size_t prow = (((size_t)bh * p.nrb + blk.rb) * p.zmax + blk.z) * ROWS + rl;
-        *reinterpret_cast<u32x2_t*>(p.ws_ml + 2 * prow) = u32x2_t{__float_as_uint(M), __float_as_uint(L)};
-      }
+  };
+  if constexpr (RING) {
+    // Two passes of 16 rows: the wave buffers hold 16 O rows each.
+    store_o(0, col);
+    __syncthreads();  // every wave is past its tiles and its Q reads: the Q area takes (m, l)
+    store_ml();
+    __syncthreads();
+    merge_rows(std::integral_constant<int, 16>{}, 0);
+#pragma unroll
+    for (int t = 1; t < QT; ++t) {
+      __syncthreads();  // the previous pass has read the buffers
+      store_o(t, col);
+      __syncthreads();
+      merge_rows(std::integral_constant<int, 16>{}, 16 * t);
     }
+  } else {
+#pragma unroll
+    for (int t = 0; t < QT; ++t) store_o(t, 16 * t + col);
+    store_ml();
+    __syncthreads();  // every wave's O and (m, l) are in LDS
+    merge_rows(std::integral_constant<int, ROWS>{}, 0);
   }
 }
 
@@ -1115,8 +1178,10 @@ static hipError_t launch_ks_variant(const FwdParams& p, const LaunchPlan& plan, 
   X(kBf16, 256, 1, 4, 32, 1)  \
   X(kBf16, 256, 2, 2, 32, 1)  \
   X(kBf16, 256, 2, 4, 32, 2)  \
+  X(kBf16, 256, 2, 4, 32, 3)  \
   X(kBf16, 256, 1, 4, 32, 2)  \
   X(kF16, 256, 2, 4, 32, 2)   \
+  X(kF16, 256, 2, 4, 32, 3)   \
   X(kF16, 256, 1, 4, 32, 2)
 
 // (nw, kw) of a plan: kw == 1, waves on different rows; kw == nw, every wave
@@ -1150,7 +1215,8 @@ bool nvfp4_variant_exists(const LaunchPlan& l) {
                               (l.D == 256 && l.qt == 2 && l.nw == 4 && l.kw == 1 && l.bn == 32 && l.nst == 2) ||
                               (l.D == 256 && l.qt == 1 && l.nw == 4 && l.kw == 1 && l.bn == 64 && l.nst == 2) ||
                               (l.D == 256 && (l.qt == 1 || l.qt == 2) && l.nw == 4 && l.kw == 4 && l.bn == 32 &&
-                               l.nst == 2));
+                               l.nst == 2) ||
+                              (l.D == 256 && l.qt == 2 && l.nw == 4 && l.kw == 4 && l.bn == 32 && l.nst == 3));
 }
 
 template <bool CAUSAL, bool SPLIT>
@@ -1166,6 +1232,7 @@ static hipError_t launch_nvfp4(const FwdParams& p, const LaunchPlan& plan, hipSt
   if (plan.D == 64)
     return plan.bn == 128 ? launch_variant<64, 1, 4, 128, 2, 1, CAUSAL, SPLIT, kBf16, kOutNvfp4>(p, plan, stream)
                           : launch_variant<64, 1, 4, 64, 2, 1, CAUSAL, SPLIT, kBf16, kOutNvfp4>(p, plan, stream);
+  if (plan.nst == 3) return launch_ks_variant<256, 2, 4, 32, 3, CAUSAL, SPLIT, kBf16, kOutNvfp4>(p, plan, stream);
   return plan.qt == 1 ? launch_ks_variant<256, 1, 4, 32, 2, CAUSAL, SPLIT, kBf16, kOutNvfp4>(p, plan, stream)
                       : launch_ks_variant<256, 2, 4, 32, 2, CAUSAL, SPLIT, kBf16, kOutNvfp4>(p, plan, stream);
 }

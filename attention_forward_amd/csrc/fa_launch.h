@@ -67,6 +67,8 @@ struct LaunchPlan {
   int outf;                // OutFormat of the result
 };
 
+constexpr int kComputeUnits = 256;  // MI355X
+
 // Device-resident split-KV scratch of fa_fwd_static (one array per GPU,
 // in fa_kernels.hip): its size, and its address on the current device.
 constexpr size_t kStaticScratchBytes = 8u << 20;

@@ -39,7 +39,8 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 4096 FLOP/clk x 2.4 GHz)
 DEFAULT_WORKLOAD = "causal_gqa_prefill"  # the largest workload (most FLOPs and bytes)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ["attention_forward_amd/csrc/fa_kernels.hip", "attention_forward_amd/csrc/fa_api.cpp",
+KERNEL_SOURCES = ["attention_forward_amd/csrc/fa_kernels.hip", "attention_forward_amd/csrc/fa_device.h",
+                  "attention_forward_amd/csrc/fa_api.cpp",
                   "attention_forward_amd/csrc/fa_launch.h"]
 
 

@@ -249,7 +249,9 @@ int fa_fwd_nvfp4(const void* q, const void* k, const void* v, void* out_fp4, voi
  *   nw   wavefronts per workgroup  (2, 4 or 8)
  *   kw   1: the wavefronts own different rows and share the K/V tiles;
  *        nw: all wavefronts own the same rows and split the keys between
- *        them (nst must then be 1: each wavefront streams its own tiles);
+ *        them, each streaming its own tiles (nst 1: whole-tile buffers,
+ *        2: piecewise refill, 3: piecewise refill through one ring buffer
+ *        per wavefront, 80 KiB of LDS, two workgroups per compute unit);
  *        2 with nw = 4 or 8: two groups of nw/2 wavefronts on the same
  *        rows, each group sharing its own K/V tiles and taking every other
  *        key tile, merged at the end (nst 2)

@@ -191,6 +191,7 @@ CASES = {
     "d256_split_small_m": (1, 41, 1056, 8, 1, 256, False, [1009]),
     "d256_causal_split": (1, 64, 1024, 8, 1, 256, True, None),   # a chunk of new positions over a cache
     "d256_causal_single_pass": (1, 700, 700, 8, 1, 256, True, None),
+    "d256_causal_ring": (1, 1984, 1984, 8, 1, 256, True, None),  # 496 blocks: two workgroups per compute unit
     "d64_single_pass": (4, 1024, 1024, 8, 8, 64, False, None),
     "d64_split_gqa": (2, 150, 333, 6, 3, 64, False, [333, 71]),
     "d64_causal": (3, 130, 130, 4, 2, 64, True, None),
@@ -200,5 +201,5 @@ CASES = {
     "d64_32_rows_per_wave": (4, 1024, 1024, 16, 16, 64, False, None),
     "d256_16row_single_pass": (1, 512, 512, 8, 1, 256, False, [480]),
     "d256_row_split_batched": (4, 1024, 1024, 8, 1, 256, False, [968, 1024, 300, 5]),
-    "d256_row_split_64_rows": (2, 768, 768, 8, 1, 256, False, [700, 768]),
+    "d256_two_rounds": (2, 768, 768, 8, 1, 256, False, [700, 768]),  # 384 blocks: key-split ring
 }

@@ -214,7 +214,9 @@ def test_plan_kernel_choice(lib):
     # 32 rows, piecewise refill of their tile buffers); with a row block per
     # compute unit there is no split-KV ...
     assert fa.fa_fwd_plan(1, 1024, 1024, 8, 1, 256, 0) == (2, 4, 4, 32, 2, 0)
-    assert fa.fa_fwd_plan(1, 2048, 2048, 8, 1, 256, 1) == (2, 4, 4, 32, 2, 0)
+    assert fa.fa_fwd_plan(1, 2048, 2048, 8, 1, 256, 1) == (2, 4, 4, 32, 3, 0)  # 512 blocks: two per CU
+    assert fa.fa_fwd_plan(1, 1984, 1984, 8, 1, 256, 1) == (2, 4, 4, 32, 3, 0)  # 496 blocks
+    assert fa.fa_fwd_plan(1, 1536, 1536, 8, 1, 256, 1) == (2, 4, 4, 32, 2, 0)  # 384 blocks: the heaviest run alone
     # ... a padded K/V buffer runs the same plan as the unpadded keys
     assert fa.fa_fwd_plan(1, 1024, 968, 8, 1, 256, 0) == fa.fa_fwd_plan(1, 1024, 1024, 8, 1, 256, 0)
     assert fa.fa_fwd_plan(1, 41, 1009, 8, 1, 256, 0) == fa.fa_fwd_plan(1, 41, 1056, 8, 1, 256, 0)
@@ -226,7 +228,8 @@ def test_plan_kernel_choice(lib):
     assert fa.fa_fwd_plan(1, 512, 512, 8, 1, 256, 0) == (1, 4, 4, 32, 2, 0)   # 128 blocks: 16-row blocks, no split
     assert fa.fa_fwd_plan(8, 41, 1056, 8, 1, 256, 0) == (1, 4, 4, 32, 2, 0)   # 168 16-row blocks: no split
     assert fa.fa_fwd_plan(4, 1024, 1024, 8, 1, 256, 0) == (2, 4, 1, 32, 2, 0)  # 1024 blocks: row-split, 128 rows
-    assert fa.fa_fwd_plan(2, 1024, 1024, 8, 1, 256, 0) == (1, 4, 1, 64, 2, 0)  # 512 blocks: row-split, 64 rows
+    assert fa.fa_fwd_plan(2, 1024, 1024, 8, 1, 256, 0) == (2, 4, 4, 32, 3, 0)  # 512 blocks: key-split ring
+    assert fa.fa_fwd_plan(3, 700, 700, 8, 1, 256, 0) == (2, 4, 4, 32, 3, 0)    # 525 blocks: key-split ring
     assert fa.fa_fwd_plan(2, 2048, 2048, 8, 1, 256, 1) == (2, 4, 4, 32, 2, 0)  # causal keeps key-split
     # ... long key buffers (over 2048 keys): about 32 power-of-two ranges per
     # row block, 32-row workgroups unless the rows fit in 16
@@ -256,7 +259,8 @@ def test_variant_rejections(lib):
     args = [Q, K, V, O, L, 1, 64, 64, 8, 1, 256, 0, 0, 0.0625]
     assert fa.fa_fwd_variant(*args, 3, 4, 1, 64, 2, 0, 0) == fa.FA_ERR_UNSUPPORTED   # not compiled
     assert fa.fa_fwd_variant(*args, 1, 4, 1, 32, 3, 0, 0) == fa.FA_ERR_UNSUPPORTED   # no 3-stage build
-    assert fa.fa_fwd_variant(*args, 2, 4, 4, 32, 3, 0, 0) == fa.FA_ERR_UNSUPPORTED   # key-split: nst 1 or 2
+    assert fa.fa_fwd_variant(*args, 1, 4, 4, 32, 3, 0, 0) == fa.FA_ERR_UNSUPPORTED   # key-split ring: 32 rows only
+    assert fa.fa_fwd_variant(*args, 2, 4, 4, 32, 4, 0, 0) == fa.FA_ERR_UNSUPPORTED   # key-split: nst 1 to 3
     assert fa.fa_fwd_variant(*args, 2, 4, 4, 64, 2, 0, 0) == fa.FA_ERR_UNSUPPORTED   # piecewise: 32-key tiles only
     assert fa.fa_fwd_variant(*args, 2, 4, 2, 32, 1, 0, 0) == fa.FA_ERR_UNSUPPORTED   # key groups: nst 2, not D256
     assert fa.fa_fwd_variant(*args, 1, 8, 2, 32, 2, 0, 0) == fa.FA_ERR_UNSUPPORTED   # key groups: not D256

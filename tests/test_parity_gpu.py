@@ -104,7 +104,9 @@ CASES = [
     (2, 2048, 2048, 16, 16, 72, False, [2048, 1500]),
     (8, 41, 1056, 8, 1, 256, False, [1009, 1, 0, 1056, 500, 41, 1008, 7]),   # batched action expert, no split
     (4, 1024, 1024, 8, 1, 256, False, [968, 1024, 300, 5]),                 # batched prefix: row-split D256
-    (2, 768, 768, 8, 1, 256, False, [700, 768]),                            # row-split D256, 64-key tiles
+    (2, 768, 768, 8, 1, 256, False, [700, 768]),                            # two rounds D256: key-split ring
+    (1, 1024, 1024, 16, 2, 256, False, [1000]),                             # two (batch, kv head) pairs, ring
+    (1, 2048, 2048, 8, 1, 256, True, [2000]),                               # causal ring with seqused_k
 ]
 
 

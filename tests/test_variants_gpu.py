@@ -18,13 +18,14 @@ pytestmark = pytest.mark.gpu
 # (D, qt, nw, kw, bn, nst): the variants compiled into the library.  kw = 1:
 # waves own different rows and share K/V tiles; kw = nw: waves share rows and
 # split the keys (each streams its own tiles; nst = 1: whole-tile buffers, 2:
-# piecewise refill); kw = 2 < nw: two key
+# piecewise refill, 3: piecewise refill through one ring buffer per wave, two
+# workgroups per compute unit); kw = 2 < nw: two key
 # groups of nw/2 waves, each group sharing its own tiles, merged at the end.
 VARIANTS = [(64, 1, 4, 1, 64, 2), (64, 1, 4, 1, 128, 2), (72, 1, 4, 1, 128, 2), (64, 1, 4, 1, 64, 3), (64, 2, 2, 1, 64, 2), (64, 2, 4, 1, 64, 2),
             (72, 1, 4, 1, 64, 2), (72, 1, 4, 1, 64, 3), (72, 1, 4, 1, 64, 4), (72, 2, 2, 1, 64, 2), (72, 2, 2, 1, 64, 3), (72, 2, 4, 1, 64, 2), (256, 1, 4, 1, 32, 2), (256, 1, 4, 1, 32, 4), (256, 1, 4, 1, 64, 2),
             (256, 2, 4, 1, 32, 2), (256, 2, 4, 1, 32, 4), (256, 2, 4, 1, 64, 2),
             (64, 2, 4, 4, 64, 1), (72, 2, 4, 4, 64, 1), (256, 2, 4, 4, 32, 1), (256, 1, 4, 4, 32, 1), (256, 2, 2, 2, 32, 1),
-            (256, 2, 4, 4, 32, 2), (256, 1, 4, 4, 32, 2),
+            (256, 2, 4, 4, 32, 2), (256, 2, 4, 4, 32, 3), (256, 1, 4, 4, 32, 2),
             (64, 1, 8, 2, 64, 2), (72, 1, 8, 2, 64, 2), (72, 1, 4, 2, 64, 2), (64, 1, 4, 2, 64, 2)]
 
 SHAPES = {
