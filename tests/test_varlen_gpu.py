@@ -74,6 +74,8 @@ SHAPES = [
     ([256, 100], [256, 200], 16, 16, 64),                     # two key groups of two row waves
     ([1024, 1024, 1000, 1024], [1024, 1024, 1024, 900], 16, 16, 64),  # 32 rows per wave
     ([1024, 1000, 1024, 1024], [968, 1024, 1024, 1024], 8, 1, 256),   # D256 row-split, 128 rows
+    ([768, 700], [768, 600], 8, 1, 256),                      # D256 two rounds: key-split ring
+    ([2048], [2048], 8, 1, 256),                              # one sequence of 512 blocks: ring (causal: paired)
 ]
 
 
