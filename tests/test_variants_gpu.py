@@ -87,3 +87,25 @@ def test_unknown_variant_is_rejected(gpu_device):
     with pytest.raises(fa.FAError) as e:
         _run(q, k, v, None, False, (1, 4, 1, 64, 2, 32), 0.125)  # kps not a multiple of bn
     assert e.value.code == fa.FA_ERR_UNSUPPORTED
+
+
+# The ring buffer scheme (nst 3) changes only where and when the key-split
+# kernel stages K and V; every wave computes the same tiles and the merge
+# runs in the same order, so its results equal the two-buffer scheme's
+# (nst 2) bit for bit.
+RING_CASES = [
+    (1, 2048, 2048, 8, 1, True, None),          # the causal prefill: paired row blocks
+    (1, 2048, 2048, 8, 1, True, [1900]),        # causal with fewer valid keys
+    (2, 768, 768, 8, 1, False, [700, 768]),     # two rounds, non-causal
+    (1, 200, 1000, 8, 1, False, [1000]),        # one round (unpaired)
+]
+
+
+@pytest.mark.parametrize("case", RING_CASES, ids=[str(c) for c in RING_CASES])
+def test_ring_equals_two_buffer_bitwise(gpu_device, case):
+    B, Sq, Sk, Hq, Hkv, causal, nv = case
+    print(f"ring vs two-buffer {case}", flush=True)
+    q, k, v, s = make_custom(B, Sq, Sk, Hq, Hkv, 256, seed=21, n_valid=nv)
+    o2, l2 = _run(q, k, v, s, causal, (2, 4, 4, 32, 2, 0), 1.0 / 16)
+    o3, l3 = _run(q, k, v, s, causal, (2, 4, 4, 32, 3, 0), 1.0 / 16)
+    assert torch.equal(o2, o3) and torch.equal(l2, l3)
