@@ -165,19 +165,23 @@ Plan default_plan(int B, int Sq, int Sk, int Hq, int Hkv, int D, int causal) {
       if (Sk > kps) pl.kps = kps;
     }
   }
-  if (D == 256 && !causal && pl.kps == 0 && base >= 4 * kTargetWorkgroups) {
-    // Four or more rounds of 32-row key-split blocks: every compute unit
+  if (D == 256 && !causal && pl.kps == 0 && base > 3 * kTargetWorkgroups) {
+    // More than three rounds of 32-row key-split blocks: every compute unit
     // would pull the whole K/V of its head from L2 per 32 rows.  Row-split
     // blocks of four 32-row waves share each K/V tile among 128 rows
-    // (4 x 1024 x 1024 prefix rows, 8/1 heads: 65.1 -> 46.3 us).
+    // (4 x 1024 x 1024 prefix rows, 8/1 heads: 65.1 -> 46.3 us, the ring
+    // scheme 54.0; against the ring: 896 blocks 45.3 -> 41.4 us, 960 blocks
+    // 49.9 -> 43.9 and 47.9 -> 46.2, 1000 blocks 52.9 -> 46.4).
     pl.launch.qt = 2;
     pl.launch.nw = 4;
     pl.launch.kw = 1;
     pl.launch.bn = 32;
     pl.launch.nst = 2;
   } else if (D == 256 && !causal && pl.kps == 0 && base > kTargetWorkgroups) {
-    // Two or three rounds: the key-split kernel's ring buffer scheme, two
-    // workgroups per compute unit.  Measured against row-split blocks of
+    // Up to three rounds: the key-split kernel's ring buffer scheme, two
+    // workgroups per compute unit (the 128-row row-split blocks above take
+    // 45.9 us at 768 blocks against the ring's 41.7, 40.7 against 34.5 at
+    // 660).  Measured against row-split blocks of
     // four 16-row waves over 64-key tiles and against the two-buffer
     // key-split kernel (us per call): 2 x 768 x 768 prefix rows 25.2 / 21.5
     // -> 19.7; 2 x 1024 x 1024 32.3 / 27.2 -> 27.0; 3 x 1024 x 1024 62.9 /

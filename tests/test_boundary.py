@@ -230,6 +230,8 @@ def test_plan_kernel_choice(lib):
     assert fa.fa_fwd_plan(4, 1024, 1024, 8, 1, 256, 0) == (2, 4, 1, 32, 2, 0)  # 1024 blocks: row-split, 128 rows
     assert fa.fa_fwd_plan(2, 1024, 1024, 8, 1, 256, 0) == (2, 4, 4, 32, 3, 0)  # 512 blocks: key-split ring
     assert fa.fa_fwd_plan(3, 700, 700, 8, 1, 256, 0) == (2, 4, 4, 32, 3, 0)    # 525 blocks: key-split ring
+    assert fa.fa_fwd_plan(3, 1024, 1024, 8, 1, 256, 0) == (2, 4, 4, 32, 3, 0)  # 768 blocks: ring
+    assert fa.fa_fwd_plan(4, 896, 896, 8, 1, 256, 0) == (2, 4, 1, 32, 2, 0)    # 896 blocks: row-split, 128 rows
     assert fa.fa_fwd_plan(2, 2048, 2048, 8, 1, 256, 1) == (2, 4, 4, 32, 2, 0)  # causal keeps key-split
     # ... long key buffers (over 2048 keys): about 32 power-of-two ranges per
     # row block, 32-row workgroups unless the rows fit in 16
