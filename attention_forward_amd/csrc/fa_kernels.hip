@@ -456,6 +456,9 @@ fwd_kernel(const FwdParams p) {
 //     banks.
 // Copies of 64-byte row segments run at the full intake rate (32-byte
 // segments at about half).
+// NST == 3 (ring): the piecewise refill through one buffer per wave whose
+// slots take K and V pieces in turn (below), so that a workgroup needs
+// 80 KiB of LDS and two run on each compute unit, two waves per SIMD.
 template <int D, int QT, int KW, int BN, int NST, bool CAUSAL, bool SPLIT, int DTY, int OUTF>
 __global__ void __launch_bounds__(KW * 64, NST == 3 ? 2 : 1)
 fwd_ks_kernel(const FwdParams p) {
@@ -721,8 +724,12 @@ fwd_ks_kernel(const FwdParams p) {
     // read of tile i come only the later K(i) pieces and the V(i) pieces of
     // the earlier S^T steps; before a V read, the later V(i) pieces and the
     // K(i+1) pieces of the earlier O^T steps (none in a wave's last tile).
-    constexpr int PF = RING ? 1 : 3;   // K steps whose fragments are read ahead of their MFMAs
-    constexpr int PFV = RING ? 4 : 6;  // V fragments read ahead
+    // K steps whose fragments are read ahead of their MFMAs, and V fragments
+    // read ahead.  The ring scheme has at most 256 registers per wave (two
+    // waves per SIMD); reading K two steps ahead there makes the compiler
+    // spill inside the tile loop.
+    constexpr int PF = RING ? 1 : 3;
+    constexpr int PFV = RING ? 4 : 6;
     constexpr int WK = 2 * (G::KC - 1) + 2 * V_PIECES - 2 * PF;
     constexpr int WV = 2 * (V_PIECES - 1) + K_PIECES - PFV;
     static_assert(PFV % 2 == 0, "V reads run ahead by whole pieces");
