@@ -109,3 +109,17 @@ def test_ring_equals_two_buffer_bitwise(gpu_device, case):
     o2, l2 = _run(q, k, v, s, causal, (2, 4, 4, 32, 2, 0), 1.0 / 16)
     o3, l3 = _run(q, k, v, s, causal, (2, 4, 4, 32, 3, 0), 1.0 / 16)
     assert torch.equal(o2, o3) and torch.equal(l2, l3)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("split", [0, 1])
+def test_ring_edge_lengths(gpu_device, causal, split):
+    """The ring scheme with batch entries of no valid key, one valid key and
+    a full buffer (waves without tiles, a wave whose only tile is masked),
+    against the oracle."""
+    var = (2, 4, 4, 32, 3, 32 * split)
+    print(f"ring edge lengths causal={causal} {var}", flush=True)
+    q, k, v, s = make_custom(3, 100, 300, 8, 1, 256, seed=31, n_valid=[0, 1, 300], pad_value=float("nan"))
+    got = _run(q, k, v, s, causal, var, 1.0 / 16)
+    want = run_oracle(q, k, v, s, causal=causal, scale=1.0 / 16)
+    assert_parity(got, want, f"ring edge lengths causal={causal} {var}", strict=False)
