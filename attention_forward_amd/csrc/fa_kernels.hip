@@ -676,10 +676,11 @@ fwd_ks_kernel(const FwdParams p) {
   for (int t = 0; t < QT; ++t) {
     const int r = row0 + 16 * t + col;
     srow[t] = r < Mp ? udiv(r, g, p.g_m) + doff : -1;  // causal: the row's diagonal key
+    // (ring: read from LDS at every S^T step instead, see read_q)
+    if constexpr (!RING) {
 #pragma unroll
-    for (int c = 0; c < G::KC; ++c) {
-      const int qch = RING ? ((4 * c + grp) ^ col) : 4 * c + grp;  // row 16t + col: swizzle by col
-      qf[t][c] = G::E::cast(*reinterpret_cast<const u32x4_t*>(smem + Q_OFF + (16 * t + col) * QSTR + qch * 16));
+      for (int c = 0; c < G::KC; ++c)
+        qf[t][c] = G::E::cast(*reinterpret_cast<const u32x4_t*>(smem + Q_OFF + (16 * t + col) * QSTR + (4 * c + grp) * 16));
     }
   }
 
@@ -726,10 +727,12 @@ fwd_ks_kernel(const FwdParams p) {
     // K(i+1) pieces of the earlier O^T steps (none in a wave's last tile).
     // K steps whose fragments are read ahead of their MFMAs, and V fragments
     // read ahead.  The ring scheme has at most 256 registers per wave (two
-    // waves per SIMD); reading K two steps ahead there makes the compiler
-    // spill inside the tile loop.
-    constexpr int PF = RING ? 1 : 3;
-    constexpr int PFV = RING ? 4 : 6;
+    // waves per SIMD); it fits them, with no spills, because it reads the
+    // Q^T fragments from LDS at every step (read_q) instead of holding all
+    // 64 registers of them (holding them, it spilled around the first and
+    // last tiles even with K one step and V four fragments ahead).
+    constexpr int PF = 3;
+    constexpr int PFV = 6;
     constexpr int WK = 2 * (G::KC - 1) + 2 * V_PIECES - 2 * PF;
     constexpr int WV = 2 * (V_PIECES - 1) + K_PIECES - PFV;
     static_assert(PFV % 2 == 0, "V reads run ahead by whole pieces");
@@ -750,6 +753,13 @@ fwd_ks_kernel(const FwdParams p) {
       if (RING) return 2 * (V_PIECES - 1 - (d_read >> 1)) + (last || d_read < PFV ? 0 : 2 * ((d_read - PFV) >> 1));
       if (last) return 2 * (V_PIECES - 1 - (d_read >> 1));
       return first ? 2 + 4 * (V_PIECES - 1 - (d_read >> 1)) + 2 * (d_read >= PFV ? (d_read - PFV) >> 1 : 0) : WV;
+    };
+    // Ring: Q^T fragment of row 16t + col, head-dim step c (16-byte chunk
+    // 4c + grp of the row, swizzled by the row).  The Q tile stays in LDS
+    // until the merge, so the ring reads it at every S^T step instead of
+    // holding all of Q^T in registers.
+    auto read_q = [&](int c, int t) __attribute__((always_inline)) -> typename G::E::v8 {
+      return G::E::cast(*reinterpret_cast<const u32x4_t*>(smem + Q_OFF + (16 * t + col) * QSTR + (((4 * c + grp) ^ col) * 16)));
     };
     auto read_k = [&](int c, int mt) __attribute__((always_inline)) -> typename G::E::v8 {
       return G::E::cast(*reinterpret_cast<const u32x4_t*>(kb + (c * G::MT + mt) * 1024));
@@ -774,27 +784,38 @@ fwd_ks_kernel(const FwdParams p) {
 #pragma unroll
         for (int t = 0; t < QT; ++t) sacc[mt][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       typename G::E::v8 kf[G::KC][G::MT];
+      typename G::E::v8 qs[G::KC][QT];  // ring: Q^T fragments of the steps read ahead
       wait_vm(k_wait(FIRST, LAST, PF - 1));
 #pragma unroll
-      for (int c = 0; c < PF; ++c)
+      for (int c = 0; c < PF; ++c) {
 #pragma unroll
         for (int mt = 0; mt < G::MT; ++mt) kf[c][mt] = read_k(c, mt);
+        if constexpr (RING) {
+#pragma unroll
+          for (int t = 0; t < QT; ++t) qs[c][t] = read_q(c, t);
+        }
+      }
 #pragma unroll
       for (int c = 0; c < G::KC; ++c) {
         if (c + PF < G::KC) {
           wait_vm(k_wait(FIRST, LAST, c + PF));
 #pragma unroll
           for (int mt = 0; mt < G::MT; ++mt) kf[c + PF][mt] = read_k(c + PF, mt);
+          if constexpr (RING) {
+#pragma unroll
+            for (int t = 0; t < QT; ++t) qs[c + PF][t] = read_q(c + PF, t);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
-          for (int t = 0; t < QT; ++t) sacc[mt][t] = G::E::mfma(kf[c][mt], qf[t][c], sacc[mt][t]);
+          for (int t = 0; t < QT; ++t) sacc[mt][t] = G::E::mfma(kf[c][mt], RING ? qs[c][t] : qf[t][c], sacc[mt][t]);
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (RING) {
-          // the reads of K slot c have returned: V(i) piece c goes into it
-          wait_lgkm(2 * (G::KC - 1 - c < PF ? G::KC - 1 - c : PF));
+          // the reads of K slot c (and of its Q fragments) have returned:
+          // V(i) piece c goes into it
+          wait_lgkm((2 + QT) * (G::KC - 1 - c < PF ? G::KC - 1 - c : PF));
           copy_v_piece((uint32_t)kt * rstride_v, c, 0);
           copy_v_piece((uint32_t)kt * rstride_v, c, 1);
         } else if constexpr (FIRST) {
